@@ -1,0 +1,134 @@
+/*
+ * pfkv: split-KV attention for the speculative-decoding verify step over a paged
+ * fp8 KV cache, native to MI355X (gfx950 / CDNA4).
+ *
+ * The operation (aiter PR #5190 "gfx950 assembly MTP-verify attention for
+ * head_dim 256 fp8 paged KV", sections Motivation, Modifications, Kernel notes and
+ * Supported; SGLang PR #37465 "gfx950 assembly attention for EAGLE verify, draft
+ * extend and decode", section Modifications): for each sequence b with q_len n_b
+ * query tokens (1..4) and KV length L_b, every query head attends with a softmax
+ * to the first L_b positions of the paged fp8 KV cache, query i (0-based) seeing
+ * positions 0 .. L_b - n_b + i (a causal mask over the last n_b positions). The
+ * cache is NHD with 16-token pages and head_dim 256; K and V are e4m3fn bytes
+ * whose real values are byte * k_descale (resp. v_descale); G = Hq / Hkv query
+ * heads (16 or 8) share each KV head, query head hq reading KV head hq / G. The
+ * context of each sequence is cut into num_segments KV segments processed
+ * independently; each writes partial softmax statistics to the workspace and a
+ * second kernel merges them by log-sum-exp into the bf16 output.
+ *
+ * Threading / ownership: every buffer is owned by the caller and lives in device
+ * memory of the current HIP device. The library allocates nothing per call,
+ * never reads device memory from the host and never synchronizes: calls only
+ * enqueue kernels on the given stream, so they are safe to capture in a HIP
+ * graph. Device properties are cached per device on first use.
+ */
+#ifndef PFKV_H_
+#define PFKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point (0 = success). */
+enum pfkv_status {
+  PFKV_OK = 0,
+  PFKV_INVALID = 1,     /* null pointer, bad size, bad stride, too-small workspace, non-finite scale */
+  PFKV_UNSUPPORTED = 2, /* valid request outside what the kernels serve: the caller should fall back */
+  PFKV_DEVICE = 3,      /* a pointer is not device memory of the current device */
+  PFKV_LAUNCH = 4       /* a HIP runtime error (its text is in pfkv_last_error) */
+};
+
+/* Arguments of one verify-attention call. Device pointers first, then host values. */
+typedef struct pfkv_args {
+  const void* q;               /* bf16 [total_q, num_q_heads, head_dim], strides below, unit last stride */
+  const void* k_cache;         /* e4m3fn bytes [num_pages, page_size, num_kv_heads, head_dim], contiguous */
+  const void* v_cache;         /* same layout as k_cache */
+  const int32_t* block_tables; /* [num_seqs, block_table_stride]; entries in [0, num_pages) */
+  const int32_t* seq_lens;     /* [num_seqs]: L_b, the KV length including the n_b query tokens */
+  const int32_t* cu_seqlens_q; /* [num_seqs + 1]: prefix sums of n_b, cu[0] = 0, cu[num_seqs] = total_q */
+  const float* k_descale;      /* one fp32 element */
+  const float* v_descale;      /* one fp32 element */
+  void* workspace;             /* >= pfkv_workspace_bytes(num_segments, total_q, num_q_heads) bytes, 16-B aligned */
+  void* out;                   /* bf16 [total_q, num_q_heads, head_dim], strides below, unit last stride */
+  int64_t q_stride_token;      /* elements between consecutive tokens of q */
+  int64_t q_stride_head;       /* elements between consecutive heads of q */
+  int64_t out_stride_token;
+  int64_t out_stride_head;
+  int64_t block_table_stride;  /* elements between rows of block_tables (>= max_pages_per_seq) */
+  uint64_t workspace_size;     /* bytes available at workspace */
+  int32_t num_seqs;            /* N >= 1 */
+  int32_t total_q;             /* T = cu_seqlens_q[N], 1 <= T <= 4 N */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;            /* must be 256 */
+  int32_t page_size;           /* must be 16 */
+  int32_t num_pages;           /* pages in k_cache / v_cache */
+  int32_t max_pages_per_seq;   /* columns of block_tables that may be read */
+  int32_t num_segments;        /* S in [1, 64] */
+  float softmax_scale;         /* multiplies q . k (after descale); finite and > 0 */
+} pfkv_args;
+
+/*
+ * Pure host-side validation; reads no device memory and needs no GPU.
+ * arch: the device's gcnArchName (e.g. "gfx950:sramecc+:xnack-"); anything not
+ * starting with "gfx950" is PFKV_UNSUPPORTED. num_cus: compute units (> 0).
+ * Returns a pfkv_status; on failure pfkv_last_error() says which check failed.
+ * Device-side preconditions that are NOT checked here (they would need a device
+ * read): 0 <= n_b <= 4, n_b <= L_b <= page_size * max_pages_per_seq, and block
+ * table entries in [0, num_pages). The kernels clamp each of them so that no
+ * access leaves its buffer; results for inputs that break them are unspecified.
+ */
+int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
+
+/*
+ * Enqueue the verify-attention call on `stream` (a hipStream_t; NULL = the null
+ * stream): the split-KV main kernel on a grid of num_segments x num_seqs x
+ * num_kv_heads work-groups, then the segment reduce. Validates with
+ * pfkv_check_args against the current device first and checks that the device
+ * pointers belong to it. Aliasing between out and any input is not allowed.
+ * Concurrent calls that share a workspace race; give each stream its own.
+ */
+int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);
+
+/*
+ * Segment-count heuristic (aiter PR #5190, Modifications: a helper that picks
+ * the number of segments; Kernel notes: one work-group per CU):
+ * clamp(num_cus / (num_seqs * num_kv_heads), 1, 64). Pure; returns 0 for
+ * non-positive inputs.
+ */
+int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
+
+/* Workspace bytes for S segments: S * total_q * num_q_heads * (head_dim 256 + 2) * 4. 0 for bad sizes. */
+uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads);
+
+/* Text of the most recent failure on this host thread ("" if none). Valid until the next call. */
+const char* pfkv_last_error(void);
+
+/*
+ * Properties of HIP device `device` as the library caches them: its gcnArchName
+ * (copied NUL-terminated into arch, at most arch_len bytes) and CU count.
+ */
+int pfkv_device_info(int device, char* arch, int arch_len, int* num_cus);
+
+/*
+ * Streaming-read microbenchmark kernels (aiter PR #5190, Microbenchmark: a
+ * streaming-read microbenchmark that bounds the achievable read rate). Reads
+ * `bytes` bytes of `buf` once and writes a checksum word to `sink` (4 bytes of
+ * device memory) so the reads cannot be elided.
+ *   variant 0: contiguous 16-byte vector loads into registers, grid-stride;
+ *   variant 1: contiguous 4 KiB pages through LDS with global_load_lds_dwordx4;
+ *   variant 2: as 1, visiting pages in the order given by page_order
+ *              (num_pages int32 page indices in [0, bytes / 4096)).
+ * bytes must be a positive multiple of 4096 for variants 1 and 2 and of 16 for 0.
+ */
+int pfkv_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,
+                     int64_t num_pages, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFKV_H_ */

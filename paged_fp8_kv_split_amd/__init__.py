@@ -1,0 +1,17 @@
+"""Split-KV verify attention over a paged fp8 KV cache, native to MI355X (gfx950).
+
+The compute path is the HIP library ``libpfkv.so`` built from ``csrc/``; the
+Python side only marshals arguments to its C ABI (see ``binding.py``). The
+library is loaded on first use and a missing build raises ``RuntimeError``:
+there is no CPU fallback.
+"""
+
+from .binding import (  # noqa: F401
+    PfkvError,
+    library_path,
+    load_library,
+    num_segments,
+    stream_read,
+    verify_attn,
+    workspace_bytes,
+)

@@ -1,0 +1,250 @@
+"""ctypes binding of ``libpfkv.so``: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI declared
+in ``include/pfkv.h``; torch is used here for device memory (``out`` and the
+workspace) and for the current stream. There is no fallback: if the library is
+not built, or a call fails, a Python exception is raised.
+
+The call mirrors ``mtp_verify_attn_fwd_asm(q, k_cache, v_cache, block_tables,
+seq_lens, cu_seqlens_q, k_descale, v_descale, softmax_scale, num_segments=None,
+out=None)`` of aiter PR #5190 ("gfx950 assembly MTP-verify attention for head_dim
+256 fp8 paged KV"), section Modifications.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpfkv.so"
+_lib = None
+
+STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "DEVICE", 4: "LAUNCH"}
+
+
+class PfkvError(RuntimeError):
+    """A non-zero status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pfkv {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class PfkvArgs(ctypes.Structure):
+    """Mirror of ``pfkv_args`` in include/pfkv.h (same field order and types)."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("k_descale", ctypes.c_void_p),
+        ("v_descale", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("q_stride_token", ctypes.c_int64),
+        ("q_stride_head", ctypes.c_int64),
+        ("out_stride_token", ctypes.c_int64),
+        ("out_stride_head", ctypes.c_int64),
+        ("block_table_stride", ctypes.c_int64),
+        ("workspace_size", ctypes.c_uint64),
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load ``libpfkv.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                           "from the repository root")
+    lib = ctypes.CDLL(path)
+    lib.pfkv_check_args.argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_char_p, ctypes.c_int]
+    lib.pfkv_check_args.restype = ctypes.c_int
+    lib.pfkv_verify_attn_fwd.argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
+    lib.pfkv_verify_attn_fwd.restype = ctypes.c_int
+    lib.pfkv_num_segments.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.pfkv_num_segments.restype = ctypes.c_int
+    lib.pfkv_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.pfkv_workspace_bytes.restype = ctypes.c_uint64
+    lib.pfkv_last_error.argtypes = []
+    lib.pfkv_last_error.restype = ctypes.c_char_p
+    lib.pfkv_device_info.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.pfkv_device_info.restype = ctypes.c_int
+    lib.pfkv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pfkv_stream_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _raise_on(status: int):
+    if status != 0:
+        msg = load_library().pfkv_last_error()
+        raise PfkvError(status, msg.decode() if msg else "")
+
+
+def last_error() -> str:
+    msg = load_library().pfkv_last_error()
+    return msg.decode() if msg else ""
+
+
+def device_info(device: Optional[int] = None):
+    """(gcnArchName, CU count) of a HIP device as the library sees it."""
+    if device is None:
+        device = torch.cuda.current_device()
+    buf = ctypes.create_string_buffer(128)
+    cus = ctypes.c_int(0)
+    _raise_on(load_library().pfkv_device_info(int(device), buf, 128, ctypes.byref(cus)))
+    return buf.value.decode(), cus.value
+
+
+def num_segments(num_cus: int, num_seqs: int, num_kv_heads: int) -> int:
+    """The library's segment-count heuristic (one work-group per CU)."""
+    return int(load_library().pfkv_num_segments(int(num_cus), int(num_seqs), int(num_kv_heads)))
+
+
+def workspace_bytes(num_segments_: int, total_q: int, num_q_heads: int) -> int:
+    return int(load_library().pfkv_workspace_bytes(int(num_segments_), int(total_q), int(num_q_heads)))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _as_bytes(cache: torch.Tensor) -> torch.Tensor:
+    if cache.dtype == torch.float8_e4m3fn:
+        return cache.view(torch.uint8)
+    if cache.dtype != torch.uint8:
+        raise TypeError(f"KV cache must be float8_e4m3fn or uint8 codes, got {cache.dtype}")
+    return cache
+
+
+def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
+               softmax_scale, num_segments_, out, workspace) -> PfkvArgs:
+    """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here)."""
+    k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
+        raise TypeError("q must be bf16 [T, Hq, D] with unit last stride")
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or out.stride(2) != 1:
+        raise TypeError("out must be bf16 with q's shape and unit last stride")
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise TypeError("k_cache / v_cache must be [num_pages, page_size, Hkv, D] of equal shape")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise TypeError("k_cache / v_cache must be contiguous")
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("cu_seqlens_q", cu_seqlens_q)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise TypeError("block_tables must be [N, max_pages] with unit column stride")
+    if not (seq_lens.is_contiguous() and cu_seqlens_q.is_contiguous()):
+        raise TypeError("seq_lens / cu_seqlens_q must be contiguous")
+    for name, t in (("k_descale", k_descale), ("v_descale", v_descale)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != 1:
+            raise TypeError(f"{name} must be a one-element float32 tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+                    ("seq_lens", seq_lens), ("cu_seqlens_q", cu_seqlens_q), ("out", out),
+                    ("workspace", workspace)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    a = PfkvArgs()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.block_tables, a.seq_lens, a.cu_seqlens_q = (block_tables.data_ptr(), seq_lens.data_ptr(),
+                                                  cu_seqlens_q.data_ptr())
+    a.k_descale, a.v_descale = k_descale.data_ptr(), v_descale.data_ptr()
+    a.workspace, a.out = workspace.data_ptr(), out.data_ptr()
+    a.q_stride_token, a.q_stride_head = q.stride(0), q.stride(1)
+    a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1)
+    a.block_table_stride = block_tables.stride(0)
+    a.workspace_size = workspace.numel()
+    a.num_seqs = seq_lens.numel()
+    a.total_q = q.shape[0]
+    a.num_q_heads = q.shape[1]
+    a.num_kv_heads = k_cache.shape[2]
+    a.head_dim = q.shape[2]
+    a.page_size = k_cache.shape[1]
+    a.num_pages = k_cache.shape[0]
+    a.max_pages_per_seq = block_tables.shape[1]
+    a.num_segments = int(num_segments_)
+    a.softmax_scale = float(softmax_scale)
+    return a
+
+
+def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
+                softmax_scale, num_segments=None, out=None, workspace=None, stream=None):
+    """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``).
+
+    ``num_segments=None`` picks the library heuristic from the device's CU count.
+    ``workspace`` (uint8, at least :func:`workspace_bytes` bytes) is allocated with
+    torch when not given. The call is enqueued on ``stream`` (default: torch's
+    current stream) and does not synchronize.
+    """
+    lib = load_library()
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    if num_segments is None:
+        _, cus = device_info(q.device.index)
+        num_segments = num_segments_for(cus, seq_lens.numel(), k_cache.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = workspace_bytes(num_segments, q.shape[0], q.shape[1])
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
+                   softmax_scale, num_segments, out, workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _raise_on(lib.pfkv_verify_attn_fwd(ctypes.byref(a), ctypes.c_void_p(handle)))
+    return out
+
+
+def num_segments_for(num_cus: int, num_seqs: int, num_kv_heads: int) -> int:
+    return num_segments(num_cus, num_seqs, num_kv_heads)
+
+
+def check_args(args: PfkvArgs, arch: str = "gfx950:sramecc+:xnack-", num_cus: int = 256) -> int:
+    """Run the library's pure host validation (no GPU needed); returns the status."""
+    return int(load_library().pfkv_check_args(ctypes.byref(args), arch.encode(), int(num_cus)))
+
+
+def stream_read(buf: torch.Tensor, variant: int, page_order: Optional[torch.Tensor] = None,
+                sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Launch one streaming-read pass over ``buf`` (see ``pfkv_stream_read``)."""
+    lib = load_library()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    n_pages = 0 if page_order is None else page_order.numel()
+    _raise_on(lib.pfkv_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                   int(variant), ctypes.c_void_p(_ptr(page_order) or 0), n_pages,
+                                   ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(handle)))
+    return sink
