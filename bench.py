@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of split-KV verify attention over a paged fp8 KV cache on one MI355X.
+
+Metric: effective KV-read bandwidth = sum_b L_b * Hkv * 256 * 2 bytes / time per
+call (split-KV main kernel + segment reduce), at cold L2: R independent replicas
+of the inputs (data and randomly permuted page tables) are rotated call by call,
+so every call streams its K/V from HBM (aiter PR #5190, Microbenchmark).
+
+Default workload: 16 sequences x 35000 context, q_len 4 with a causal mask, 16
+query heads on 1 KV head, head_dim 256, fp8 e4m3 page-16 NHD K/V, 16 segments,
+16 replicas. Prints one JSON line on stdout; progress goes to stderr.
+
+The timed region is exactly --steps back-to-back calls between two HIP events on
+the launch stream, after --warmup untimed calls. A second, instrumented pass of
+the same length records events around every main-kernel launch to get that
+kernel's average duration for the roofline. The streaming-read ceiling and the
+CPU oracle (on a bounded sample) are measured in the same run.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective KV-read TB/s (and us/call) at 16 seqs x 35k ctx, GQA 16, hd256 fp8"
+HBM_PEAK_GBPS = 8000.0
+# The pages' gfx950 assembly kernel + reduce on this workload: 67 us per call,
+# i.e. 286.72 MB / 67 us = 4.28 TB/s under the same bytes / time formula.
+PAGES_TBPS = 286.72e6 / 67e-6 / 1e12
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "splitkv_main_prod_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    path = os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", "splitkv_main.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per main-kernel launch from committed rocprofv3 counters, if current."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def stream_ceiling(pfkv, torch, gib=4, reps=5):
+    """Best-of-reps read rate (TB/s) of the three streaming-read variants."""
+    nbytes = gib << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    order = torch.randperm(nbytes // 4096, device="cuda").to(torch.int32)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {}
+    for variant, name in ((0, "contiguous_vector"), (1, "contiguous_lds_dma"), (2, "random_page_lds_dma")):
+        pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None, sink=sink)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None, sink=sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        res[name] = round(nbytes / best / 1e12, 4)
+    del buf, order
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_oracle_baseline(case, kv_bytes_per_call, min_seconds=10.0, max_reps=3):
+    """Time the numpy oracle on host cores over whole calls of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    # host copy of just the pages the sequences use, with remapped block tables
+    lens = case.seq_lens.cpu().numpy()
+    bt = case.block_tables.cpu().numpy()
+    page = case.k_cache.shape[1]
+    ids, rows = [], []
+    for b, L in enumerate(lens):
+        n = -(-int(L) // page)
+        rows.append(list(range(len(ids), len(ids) + n)))
+        ids.extend(int(x) for x in bt[b, :n])
+    table = np.zeros((len(lens), max(len(r) for r in rows)), np.int32)
+    for b, r in enumerate(rows):
+        table[b, :len(r)] = r
+    idx = torch.tensor(ids, dtype=torch.long, device=case.k_cache.device)
+    host = dict(q=case.q.cpu().view(torch.int16).numpy().view(np.uint16),
+                k_cache=case.k_cache[idx].cpu().numpy(), v_cache=case.v_cache[idx].cpu().numpy(),
+                block_tables=table, seq_lens=lens, cu_seqlens_q=case.cu_seqlens_q.cpu().numpy(),
+                k_descale=float(case.k_descale.item()), v_descale=float(case.v_descale.item()),
+                softmax_scale=case.softmax_scale)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing or unreadable
+        blas = 1
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.attend(**host)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv_bytes_per_call * reps / dt / 1e12, 8), "unit": "TB/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"{reps} whole call(s) of the benchmark workload (replica 0), {dt:.1f} s wall, "
+                      f"{dt / reps:.2f} s per call; fp64 numpy with BLAS threads={blas}, "
+                      f"affinity cpus={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="prod")
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--segments", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_fp8_kv_split_amd as pfkv
+    from paged_fp8_kv_split_amd import binding
+    from paged_fp8_kv_split_amd.workloads import make_case, workload
+
+    if not os.path.exists(pfkv.library_path()):
+        from paged_fp8_kv_split_amd.build import build
+        build()
+    lib = pfkv.load_library()
+    torch.cuda.init()
+    arch, cus = binding.device_info(0)
+    w = workload(args.workload)
+    R = args.replicas or w.replicas
+    S = args.segments or w.num_segments or pfkv.num_segments(cus, w.num_seqs, w.num_kv_heads)
+    log(f"device {arch}, {cus} CUs; workload {w.name}: {w.num_seqs} seqs, ctx {w.ctx[:4]}..., "
+        f"q_lens {w.q_lens[:4]}..., Hq {w.num_q_heads} / Hkv {w.num_kv_heads}, S={S}, replicas={R}")
+
+    t0 = time.perf_counter()
+    cases = [make_case(w, "cuda", replica=r) for r in range(R)]
+    torch.cuda.synchronize()
+    log(f"generated {R} replicas in {time.perf_counter() - t0:.1f} s")
+
+    T, Hq = w.total_q, w.num_q_heads
+    out = torch.empty((T, Hq, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device="cuda")
+    argv = [binding.build_args(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.cu_seqlens_q,
+                               c.k_descale, c.v_descale, c.softmax_scale, S, out, ws) for c in cases]
+    refs = [ctypes.byref(a) for a in argv]
+    stream = torch.cuda.current_stream()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(k):
+        st = lib.pfkv_verify_attn_fwd(refs[k % R], handle)
+        if st != 0:
+            raise binding.PfkvError(st, binding.last_error())
+
+    for k in range(args.warmup):
+        call(k)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly --steps calls
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    ev0.record(stream)
+    for k in range(args.steps):
+        call(k)
+    ev1.record(stream)
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    us_per_call = total_ms * 1e3 / args.steps
+    tbps = w.kv_bytes / (us_per_call * 1e-6) / 1e12
+    log(f"{args.steps} calls: {us_per_call:.2f} us/call, {tbps:.3f} TB/s effective "
+        f"(host {host_s * 1e6 / args.steps:.1f} us/call to enqueue)")
+
+    # ---- instrumented pass: events around each main-kernel launch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for k in range(args.steps):
+        starts[k].record(stream)
+        st = lib.pfkv_splitkv_main(refs[k % R], handle)
+        ends[k].record(stream)
+        st |= lib.pfkv_segment_reduce(refs[k % R], handle)
+        if st != 0:
+            raise binding.PfkvError(st, binding.last_error())
+    torch.cuda.synchronize()
+    main_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) * 1e3 / args.steps
+    achieved_gbps = w.kv_bytes / (main_us * 1e-6) / 1e9
+    log(f"main kernel alone: {main_us:.2f} us/launch, {achieved_gbps / 1e3:.3f} TB/s")
+
+    ceiling = None
+    if not args.no_ceiling:
+        del cases[1:]
+        torch.cuda.empty_cache()
+        ceiling = stream_ceiling(pfkv, torch)
+        log(f"streaming-read ceiling: {ceiling}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_oracle_baseline(cases[0], w.kv_bytes)
+        log(f"cpu oracle: {cpu}")
+
+    best_ceiling = max(ceiling.values()) if ceiling else None
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "us_per_call": round(us_per_call, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tbps / PAGES_TBPS, 4) if w.name == "prod" else None,
+        "dtype": "fp8-e4m3 K/V bytes; bf16 QK and fp16 PV MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.num_seqs} seqs x ctx {w.ctx[0] if len(set(w.ctx)) == 1 else list(w.ctx)}, "
+                        f"q_len {w.q_lens[0] if len(set(w.q_lens)) == 1 else list(w.q_lens)} causal, "
+                        f"{w.num_q_heads} q heads / {w.num_kv_heads} kv head(s), head_dim {w.head_dim}, "
+                        f"page {w.page_size} NHD fp8 e4m3, per-tensor descales",
+            "num_segments": S,
+            "replicas": R,
+            "kv_bytes_per_call": w.kv_bytes,
+            "device": arch,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "splitkv_main_kernel",
+            "achieved": round(achieved_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "main_kernel_us": round(main_us, 2),
+        },
+        "ceiling_TBps": ceiling,
+        "frac_of_measured_ceiling": round(tbps / best_ceiling, 4) if best_ceiling else None,
+        "frac_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBPS, 4),
+        "pages_asm_TBps_same_formula": round(PAGES_TBPS, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,6 +94,17 @@ int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
 int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);
 
 /*
+ * The two stages of pfkv_verify_attn_fwd, exposed separately (same arguments,
+ * same validation) so that a caller can place or time them individually:
+ * pfkv_splitkv_main enqueues only the split-KV main kernel, which writes the
+ * per-segment partials to the workspace; pfkv_segment_reduce enqueues only the
+ * reduce that turns the workspace into out. Running them in this order on one
+ * stream is exactly pfkv_verify_attn_fwd.
+ */
+int pfkv_splitkv_main(const pfkv_args* args, void* stream);
+int pfkv_segment_reduce(const pfkv_args* args, void* stream);
+
+/*
  * Segment-count heuristic (aiter PR #5190, Modifications: a helper that picks
  * the number of segments; Kernel notes: one work-group per CU):
  * clamp(num_cus / (num_seqs * num_kv_heads), 1, 64). Pure; returns 0 for

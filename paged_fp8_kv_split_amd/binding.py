@@ -85,6 +85,9 @@ def load_library():
     lib.pfkv_check_args.restype = ctypes.c_int
     lib.pfkv_verify_attn_fwd.argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
     lib.pfkv_verify_attn_fwd.restype = ctypes.c_int
+    for name in ("pfkv_splitkv_main", "pfkv_segment_reduce"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
+        getattr(lib, name).restype = ctypes.c_int
     lib.pfkv_num_segments.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.pfkv_num_segments.restype = ctypes.c_int
     lib.pfkv_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]

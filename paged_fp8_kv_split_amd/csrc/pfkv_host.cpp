@@ -1,0 +1,310 @@
+// C ABI of libpfkv (declared in include/pfkv.h): argument validation, the
+// segment-count heuristic, device-property caching and the two launches.
+//
+// The call mirrors mtp_verify_attn_fwd(...) / mtp_verify_attn_fwd_asm(...) and
+// mtp_verify_attn_num_segments() of aiter PR #5190 ("gfx950 assembly MTP-verify
+// attention for head_dim 256 fp8 paged KV"), section Modifications; what is
+// accepted follows its section Supported (gfx950, head_dim 256, page 16, e4m3
+// per-tensor K/V, bf16 Q, GQA 16 or 8) with q_len 1..4 per sequence as in SGLang
+// PR #37465, Modifications. Unsupported shapes return PFKV_UNSUPPORTED so that a
+// caller can fall back, as the SGLang entry points do.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pfkv.h"
+#include "pfkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+struct DeviceProps {
+  bool valid = false;
+  std::string arch;
+  int num_cus = 0;
+};
+
+std::mutex g_props_mu;
+std::vector<DeviceProps> g_props;
+
+int cached_props(int device, DeviceProps* out) {
+  std::lock_guard<std::mutex> lock(g_props_mu);
+  if (device < 0) return fail(PFKV_INVALID, "negative device index");
+  if ((size_t)device >= g_props.size()) g_props.resize(device + 1);
+  DeviceProps& d = g_props[device];
+  if (!d.valid) {
+    hipDeviceProp_t prop;
+    const hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PFKV_LAUNCH, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    }
+    d.arch = prop.gcnArchName;
+    d.num_cus = prop.multiProcessorCount;
+    d.valid = true;
+  }
+  *out = d;
+  return PFKV_OK;
+}
+
+bool is_gfx950(const char* arch) {
+  return std::strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':');
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_device_pointer(const void* ptr, int device, const char* name) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_DEVICE, std::string(name) + " is not memory known to HIP");
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(PFKV_DEVICE, std::string(name) + " is not device memory");
+  if (attr.device != device)
+    return fail(PFKV_DEVICE, std::string(name) + " belongs to device " + std::to_string(attr.device) +
+                                 ", not the current device " + std::to_string(device));
+  return PFKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pfkv_last_error(void) { return g_last_error.c_str(); }
+
+int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads) {
+  if (num_cus <= 0 || num_seqs <= 0 || num_kv_heads <= 0) return 0;
+  const long long per = (long long)num_seqs * num_kv_heads;
+  long long s = num_cus / per;
+  if (s < 1) s = 1;
+  if (s > pfkv::kMaxSegments) s = pfkv::kMaxSegments;
+  return (int)s;
+}
+
+uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads) {
+  if (num_segments <= 0 || total_q <= 0 || num_q_heads <= 0) return 0;
+  return (uint64_t)num_segments * (uint64_t)total_q * (uint64_t)num_q_heads * (pfkv::kHeadDim + 2) * 4u;
+}
+
+int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
+  g_last_error.clear();
+  if (a == nullptr) return fail(PFKV_INVALID, "args is NULL");
+  if (arch == nullptr) return fail(PFKV_INVALID, "arch is NULL");
+  if (num_cus <= 0) return fail(PFKV_INVALID, "num_cus must be positive");
+
+  const struct { const void* p; const char* name; } ptrs[] = {
+      {a->q, "q"}, {a->k_cache, "k_cache"}, {a->v_cache, "v_cache"}, {a->block_tables, "block_tables"},
+      {a->seq_lens, "seq_lens"}, {a->cu_seqlens_q, "cu_seqlens_q"}, {a->k_descale, "k_descale"},
+      {a->v_descale, "v_descale"}, {a->workspace, "workspace"}, {a->out, "out"}};
+  for (const auto& x : ptrs)
+    if (x.p == nullptr) return fail(PFKV_INVALID, std::string(x.name) + " is NULL");
+
+  if (a->num_seqs < 1 || a->num_seqs > (1 << 20)) return fail(PFKV_INVALID, "num_seqs must be in [1, 2^20]");
+  if (a->total_q < 1) return fail(PFKV_INVALID, "total_q must be >= 1");
+  if ((int64_t)a->total_q > (int64_t)pfkv::kMaxQLen * a->num_seqs)
+    return fail(PFKV_INVALID, "total_q exceeds 4 query tokens per sequence");
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1) return fail(PFKV_INVALID, "head counts must be positive");
+  if (a->num_kv_heads > 4096) return fail(PFKV_INVALID, "num_kv_heads must be <= 4096");
+  if (a->num_q_heads % a->num_kv_heads != 0) return fail(PFKV_INVALID, "num_q_heads % num_kv_heads != 0");
+  if (a->num_pages < 1) return fail(PFKV_INVALID, "num_pages must be >= 1");
+  if (a->max_pages_per_seq < 1) return fail(PFKV_INVALID, "max_pages_per_seq must be >= 1");
+  if (a->max_pages_per_seq > (1 << 26)) return fail(PFKV_INVALID, "max_pages_per_seq must be <= 2^26");
+  if (a->block_table_stride < a->max_pages_per_seq)
+    return fail(PFKV_INVALID, "block_table_stride < max_pages_per_seq");
+  if (a->num_segments < 1 || a->num_segments > pfkv::kMaxSegments)
+    return fail(PFKV_INVALID, "num_segments must be in [1, 64]");
+  if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
+    return fail(PFKV_INVALID, "softmax_scale must be finite and positive");
+  if (a->q_stride_token <= 0 || a->q_stride_head <= 0 || a->out_stride_token <= 0 || a->out_stride_head <= 0)
+    return fail(PFKV_INVALID, "q / out strides must be positive");
+  if (a->q_stride_token % 8 || a->q_stride_head % 8 || !aligned(a->q, 16))
+    return fail(PFKV_INVALID, "q rows must be 16-byte aligned (strides multiple of 8 elements)");
+  if (a->out_stride_token % 4 || a->out_stride_head % 4 || !aligned(a->out, 8))
+    return fail(PFKV_INVALID, "out rows must be 8-byte aligned (strides multiple of 4 elements)");
+  if (!aligned(a->workspace, 16)) return fail(PFKV_INVALID, "workspace must be 16-byte aligned");
+  if (!aligned(a->k_cache, 16) || !aligned(a->v_cache, 16))
+    return fail(PFKV_INVALID, "k_cache / v_cache must be 16-byte aligned");
+  if (!aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4) || !aligned(a->cu_seqlens_q, 4) ||
+      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4))
+    return fail(PFKV_INVALID, "int32 / fp32 arguments must be 4-byte aligned");
+  const uint64_t need = pfkv_workspace_bytes(a->num_segments, a->total_q, a->num_q_heads);
+  if (a->workspace_size < need)
+    return fail(PFKV_INVALID, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                  std::to_string(a->workspace_size));
+
+  // Supported envelope of the kernels.
+  if (!is_gfx950(arch)) return fail(PFKV_UNSUPPORTED, std::string("device is ") + arch + ", kernels are gfx950");
+  if (a->head_dim != pfkv::kHeadDim) return fail(PFKV_UNSUPPORTED, "head_dim must be 256");
+  if (a->page_size != pfkv::kPageSize) return fail(PFKV_UNSUPPORTED, "page_size must be 16");
+  const int group = a->num_q_heads / a->num_kv_heads;
+  if (group != 16 && group != 8)
+    return fail(PFKV_UNSUPPORTED, "query heads per KV head must be 16 or 8, got " + std::to_string(group));
+  return PFKV_OK;
+}
+
+int pfkv_device_info(int device, char* arch, int arch_len, int* num_cus) {
+  g_last_error.clear();
+  DeviceProps d;
+  const int st = cached_props(device, &d);
+  if (st != PFKV_OK) return st;
+  if (arch != nullptr && arch_len > 0) {
+    std::strncpy(arch, d.arch.c_str(), (size_t)arch_len - 1);
+    arch[arch_len - 1] = '\0';
+  }
+  if (num_cus != nullptr) *num_cus = d.num_cus;
+  return PFKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the three launch entry points; fills the kernel params.
+int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
+  g_last_error.clear();
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  }
+  DeviceProps d;
+  int st = cached_props(device, &d);
+  if (st != PFKV_OK) return st;
+  st = pfkv_check_args(a, d.arch.c_str(), d.num_cus);
+  if (st != PFKV_OK) return st;
+  const struct { const void* p; const char* name; } ptrs[] = {
+      {a->q, "q"}, {a->k_cache, "k_cache"}, {a->v_cache, "v_cache"}, {a->block_tables, "block_tables"},
+      {a->seq_lens, "seq_lens"}, {a->cu_seqlens_q, "cu_seqlens_q"}, {a->k_descale, "k_descale"},
+      {a->v_descale, "v_descale"}, {a->workspace, "workspace"}, {a->out, "out"}};
+  for (const auto& x : ptrs) {
+    st = check_device_pointer(x.p, device, x.name);
+    if (st != PFKV_OK) return st;
+  }
+
+  const int group = a->num_q_heads / a->num_kv_heads;
+  float* ws = (float*)a->workspace;
+  const uint64_t acc_floats = (uint64_t)a->num_segments * a->total_q * a->num_q_heads * pfkv::kHeadDim;
+
+  *mp = pfkv::MainParams();
+  *rp = pfkv::ReduceParams();
+  pfkv::MainParams& m = *mp;
+  m.q = (const uint16_t*)a->q;
+  m.q_stride_token = a->q_stride_token;
+  m.q_stride_head = a->q_stride_head;
+  m.k_cache = (const uint8_t*)a->k_cache;
+  m.v_cache = (const uint8_t*)a->v_cache;
+  m.block_tables = a->block_tables;
+  m.block_table_stride = a->block_table_stride;
+  m.seq_lens = a->seq_lens;
+  m.cu_seqlens_q = a->cu_seqlens_q;
+  m.k_descale = a->k_descale;
+  m.ws_acc = ws;
+  m.ws_ml = ws + acc_floats;
+  m.num_seqs = a->num_seqs;
+  m.total_q = a->total_q;
+  m.num_q_heads = a->num_q_heads;
+  m.num_kv_heads = a->num_kv_heads;
+  m.num_pages = a->num_pages;
+  m.max_pages_per_seq = a->max_pages_per_seq;
+  m.num_segments = a->num_segments;
+  m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
+
+  rp->ws_acc = ws;
+  rp->ws_ml = ws + acc_floats;
+  rp->v_descale = a->v_descale;
+  rp->out = (uint16_t*)a->out;
+  rp->out_stride_token = a->out_stride_token;
+  rp->out_stride_head = a->out_stride_head;
+  rp->total_q = a->total_q;
+  rp->num_q_heads = a->num_q_heads;
+  rp->num_segments = a->num_segments;
+  (void)group;
+  return PFKV_OK;
+}
+
+int launch_main(const pfkv::MainParams& mp, int group, void* stream) {
+  const hipError_t e = pfkv::launch_splitkv_main(mp, group, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("split-KV main kernel launch: ") + hipGetErrorString(e));
+  }
+  return PFKV_OK;
+}
+
+int launch_reduce(const pfkv::ReduceParams& rp, void* stream) {
+  const hipError_t e = pfkv::launch_segment_reduce(rp, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("segment reduce launch: ") + hipGetErrorString(e));
+  }
+  return PFKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pfkv_verify_attn_fwd(const pfkv_args* a, void* stream) {
+  pfkv::MainParams mp;
+  pfkv::ReduceParams rp;
+  int st = prepare(a, &mp, &rp);
+  if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
+  if (st == PFKV_OK) st = launch_reduce(rp, stream);
+  return st;
+}
+
+int pfkv_splitkv_main(const pfkv_args* a, void* stream) {
+  pfkv::MainParams mp;
+  pfkv::ReduceParams rp;
+  int st = prepare(a, &mp, &rp);
+  if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
+  return st;
+}
+
+int pfkv_segment_reduce(const pfkv_args* a, void* stream) {
+  pfkv::MainParams mp;
+  pfkv::ReduceParams rp;
+  int st = prepare(a, &mp, &rp);
+  if (st == PFKV_OK) st = launch_reduce(rp, stream);
+  return st;
+}
+
+int pfkv_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order, int64_t num_pages,
+                     void* sink, void* stream) {
+  g_last_error.clear();
+  if (buf == nullptr || sink == nullptr) return fail(PFKV_INVALID, "buf and sink must be non-NULL");
+  if (variant < 0 || variant > 2) return fail(PFKV_INVALID, "variant must be 0, 1 or 2");
+  if (bytes == 0 || bytes % (variant == 0 ? 16 : 4096)) return fail(PFKV_INVALID, "bad byte count for variant");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(PFKV_INVALID, "buf must be 16-byte aligned");
+  if (variant == 2 && (page_order == nullptr || num_pages < 1))
+    return fail(PFKV_INVALID, "variant 2 needs a page order");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) {
+    int st = check_device_pointer(buf, device, "buf");
+    if (st == PFKV_OK) st = check_device_pointer(sink, device, "sink");
+    if (st == PFKV_OK && variant == 2) st = check_device_pointer(page_order, device, "page_order");
+    if (st != PFKV_OK) return st;
+    e = pfkv::launch_stream_read(buf, bytes, variant, page_order, num_pages, (uint32_t*)sink,
+                                 (hipStream_t)stream);
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("stream read: ") + hipGetErrorString(e));
+  }
+  return PFKV_OK;
+}
+
+}  // extern "C"

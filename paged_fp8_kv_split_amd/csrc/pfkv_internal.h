@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (pfkv_host.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pfkv {
+
+constexpr int kHeadDim = 256;   // head_dim served by the kernels
+constexpr int kPageSize = 16;   // tokens per KV page
+constexpr int kMaxQLen = 4;     // query tokens per sequence
+constexpr int kMaxSegments = 64;
+
+// Workspace layout (fp32), written by the main kernel and read by the reduce:
+//   acc [S][T][Hq][256]  un-normalized sum of p * V (V without its descale)
+//   ml  [S][T][Hq][2]    (m, l): reference max in log2 units and sum of p
+// so that segment s contributes  2^(m_s - M) * acc_s / sum_s 2^(m_s - M) * l_s.
+struct MainParams {
+  const uint16_t* q;           // bf16 bits
+  int64_t q_stride_token, q_stride_head;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  int64_t block_table_stride;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  const float* k_descale;
+  float* ws_acc;
+  float* ws_ml;
+  int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
+  float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
+};
+
+struct ReduceParams {
+  const float* ws_acc;
+  const float* ws_ml;
+  const float* v_descale;
+  uint16_t* out;               // bf16 bits
+  int64_t out_stride_token, out_stride_head;
+  int32_t total_q, num_q_heads, num_segments;
+};
+
+hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
+hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,
+                              int64_t num_pages, uint32_t* sink, hipStream_t stream);
+
+}  // namespace pfkv

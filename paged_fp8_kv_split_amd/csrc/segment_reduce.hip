@@ -1,0 +1,65 @@
+// Segment reduce: merges the per-segment partials of the split-KV main kernel
+// into the bf16 output (aiter PR #5190 "gfx950 assembly MTP-verify attention for
+// head_dim 256 fp8 paged KV", section Modifications: a split-KV segment reduce
+// after the main kernel).
+//
+// For output row (t, hq) with segments s = 0 .. S-1 holding (m_s, l_s, acc_s):
+//   M = max_s m_s,  w_s = 2^(m_s - M) (0 for an empty segment, m_s = -inf),
+//   out = v_descale * sum_s w_s acc_s / sum_s w_s l_s   (0 when the sum is 0),
+// summed in the fixed order s = 0, 1, ..., then rounded to bf16 to nearest even.
+// One wave per output row, four dims per lane (coalesced 1 KiB reads per segment).
+#include "pfkv_internal.h"
+
+namespace pfkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const float const_f32;
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;   // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t rows_total = (int64_t)p.total_q * p.num_q_heads;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows_total) return;
+  const int S = p.num_segments;
+  const const_f32* ml = (const const_f32*)p.ws_ml;
+
+  float M = -__builtin_inff();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(s * rows_total + row) * 2]);
+
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float m = ml[(s * rows_total + row) * 2];
+    const float l = ml[(s * rows_total + row) * 2 + 1];
+    const float wgt = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    den += wgt * l;
+    const f32x4 a = *(const f32x4*)(p.ws_acc + (s * rows_total + row) * kHeadDim + 4 * lane);
+    num += wgt * a;
+  }
+  const float vd = *(const const_f32*)p.v_descale;
+  const float inv = den > 0.f ? vd / den : 0.f;
+  const int64_t t = row / p.num_q_heads, hq = row - t * p.num_q_heads;
+  uint16_t* dst = p.out + t * p.out_stride_token + hq * p.out_stride_head + 4 * lane;
+  const uint32_t lo = bf16_rne(num[0] * inv) | (bf16_rne(num[1] * inv) << 16);
+  const uint32_t hi = bf16_rne(num[2] * inv) | (bf16_rne(num[3] * inv) << 16);
+  *(uint2*)dst = make_uint2(lo, hi);
+}
+
+}  // namespace
+
+hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipLaunchKernelGGL(segment_reduce_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pfkv

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU tests: run the HIP path, compare with the oracle."""
+
+import numpy as np
+import torch
+
+import oracle
+import paged_fp8_kv_split_amd as pfkv
+from paged_fp8_kv_split_amd.workloads import Case
+
+# Tolerances in units of the oracle output's population std (16-bit P path).
+MAX_ERR_SIGMA = 0.15
+MEAN_ERR_SIGMA = 0.02
+
+
+def run(case: Case, num_segments=None, out=None, workspace=None):
+    return pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                            case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale,
+                            num_segments=num_segments, out=out, workspace=workspace)
+
+
+def error_stats(got: torch.Tensor, ref: np.ndarray):
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    sigma = ref.std()
+    err = np.abs(g - ref)
+    return err.max() / sigma, err.mean() / sigma
+
+
+def assert_parity(got, ref, label=""):
+    mx, mean = error_stats(got, ref)
+    print(f"[parity] {label}: max|err|/std={mx:.4f} mean|err|/std={mean:.5f}", flush=True)
+    assert mx <= MAX_ERR_SIGMA and mean <= MEAN_ERR_SIGMA, (label, mx, mean)
+    return mx, mean
+
+
+def subset(case: Case, seqs) -> Case:
+    """The sub-problem of sequences ``seqs``, with only their pages, on the host."""
+    seqs = list(seqs)
+    cu = case.cu_seqlens_q.cpu().numpy()
+    lens = case.seq_lens.cpu().numpy()
+    bt = case.block_tables.cpu().numpy()
+    page = case.k_cache.shape[1]
+    ids, tables, q_rows, new_cu = [], [], [], [0]
+    for b in seqs:
+        n_pages = -(-int(lens[b]) // page)
+        row = list(range(len(ids), len(ids) + n_pages))
+        ids.extend(int(x) for x in bt[b, :n_pages])
+        tables.append(row)
+        q_rows.extend(range(int(cu[b]), int(cu[b + 1])))
+        new_cu.append(new_cu[-1] + int(cu[b + 1] - cu[b]))
+    width = max(1, max(len(r) for r in tables))
+    table = np.zeros((len(seqs), width), np.int32)
+    for k, r in enumerate(tables):
+        table[k, :len(r)] = r
+    idx = torch.tensor(ids, dtype=torch.long, device=case.k_cache.device)
+    qidx = torch.tensor(q_rows, dtype=torch.long, device=case.q.device)
+    return Case(case.q[qidx].cpu(), case.k_cache[idx].cpu(), case.v_cache[idx].cpu(), torch.from_numpy(table),
+                torch.from_numpy(lens[seqs].astype(np.int32)), torch.tensor(new_cu, dtype=torch.int32),
+                case.k_descale.cpu(), case.v_descale.cpu(), case.softmax_scale, -1, case.workload)
+
+
+def oracle_for(case: Case) -> np.ndarray:
+    return oracle.attend(**case.to("cpu").host_arrays())
+
+
+def rows_of(case: Case, seqs):
+    cu = case.cu_seqlens_q.cpu().numpy()
+    return [t for b in seqs for t in range(int(cu[b]), int(cu[b + 1]))]

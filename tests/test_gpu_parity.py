@@ -1,0 +1,302 @@
+"""Parity of the HIP path with the CPU oracle, and its bit-exactness invariants.
+
+Every call goes through the C ABI (ctypes binding) of the in-tree libpfkv.so.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_fp8_kv_split_amd as pfkv
+from paged_fp8_kv_split_amd.workloads import Case, Workload, make_case, permute_pool, workload
+
+from gpu_util import assert_parity, error_stats, oracle_for, rows_of, run, subset
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pfkv.load_library()
+    arch, cus = pfkv.binding.device_info(0)
+    print(f"[device] {arch} CUs={cus}", flush=True)
+
+
+def _case(name, **over):
+    w = workload(name, **over)
+    return make_case(w, "cpu").to(DEV)
+
+
+# ------------------------------------------------------------------ small configs, full oracle
+@pytest.mark.parametrize("name", ["tiny", "tiny_fixed_descale", "tiny_override_descale"])
+def test_tiny_parity(name):
+    case = _case(name)
+    out = run(case, num_segments=4)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), name)
+
+
+@pytest.mark.parametrize("segments", [None, 1, 3, 7, 64])
+def test_multigroup_parity(segments):
+    case = _case("multigroup")    # 32 q heads / 2 KV heads, context 777, 2 sequences
+    out = run(case, num_segments=segments)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), f"multigroup S={segments}")
+
+
+def test_ragged_parity():
+    case = _case("ragged")        # 8 sequences, contexts 6..105000, q_len 1..4
+    print(f"[ragged] ctx={case.workload.ctx} q_lens={case.workload.q_lens}", flush=True)
+    out = run(case)               # heuristic: 32 segments on 256 CUs, empty tail segments
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), "ragged")
+
+
+def test_gqa8_three_seqs_parity():
+    w = Workload(name="g8x3", ctx=(8000, 8000, 8000), q_lens=(4, 4, 4), num_q_heads=8, num_kv_heads=1,
+                 num_segments=16, seed=31)
+    case = make_case(w, "cpu").to(DEV)
+    out = run(case, num_segments=16)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), "gqa8 3x8000")
+
+
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 16, 64])
+def test_segment_count_independence(segments):
+    w = Workload(name="s", ctx=(8000, 1234, 31), q_lens=(4, 2, 1), num_q_heads=16, num_kv_heads=1,
+                 num_segments=segments, seed=32)
+    case = make_case(w, "cpu").to(DEV)
+    ref = oracle_for(case)
+    out = run(case, num_segments=segments)
+    base = run(case, num_segments=16)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, f"S={segments}")
+    sigma = ref.std()
+    diff = (out.float() - base.float()).abs().max().item()
+    assert diff <= 0.05 * sigma, diff
+
+
+# ------------------------------------------------------------------ full-size shapes, sampled rows
+@pytest.mark.parametrize("name", ["prod", "gqa8", "long", "occupancy"])
+def test_full_size_sampled(name):
+    w = workload(name)
+    case = make_case(w, DEV)
+    out = run(case, num_segments=w.num_segments)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    seqs = [0, w.num_seqs - 1]
+    sub = subset(case, seqs)
+    ref = oracle_for(sub)
+    got = out[torch.tensor(rows_of(case, seqs), device=DEV)]
+    assert_parity(got, ref, f"{name} seqs {seqs}")
+
+
+# ------------------------------------------------------------------ workspace partials
+def test_segment_partials_match_oracle():
+    w = Workload(name="p", ctx=(3000, 300, 20), q_lens=(4, 3, 1), num_q_heads=16, num_kv_heads=1,
+                 num_segments=8, seed=33)
+    case = make_case(w, "cpu").to(DEV)
+    S, T, Hq = 8, w.total_q, w.num_q_heads
+    ws = torch.zeros(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device=DEV)
+    run(case, num_segments=S, workspace=ws)
+    torch.cuda.synchronize()
+    f = ws.view(torch.float32)
+    acc = f[: S * T * Hq * 256].view(S, T, Hq, 256).double().cpu().numpy()
+    ml = f[S * T * Hq * 256:].view(S, T, Hq, 2).double().cpu().numpy()
+    lse2, o = oracle.segment_partials(**case.to("cpu").host_arrays(), num_segments=S)
+    m, l = ml[..., 0], ml[..., 1]
+    empty = np.isneginf(lse2)
+    assert np.array_equal(empty, l == 0), "empty segments must carry l = 0"
+    assert np.all(np.isneginf(m[empty])) and np.all(acc[empty] == 0)
+    got_lse2 = m[~empty] + np.log2(l[~empty])
+    assert np.max(np.abs(got_lse2 - lse2[~empty])) < 2e-3
+    vd = float(case.v_descale.item())
+    seg_out = acc[~empty] / l[~empty][:, None] * vd
+    sigma = o[~empty].std()
+    assert np.max(np.abs(seg_out - o[~empty])) <= 0.05 * sigma
+
+
+# ------------------------------------------------------------------ bit-exact invariants
+def test_graph_replay_bitwise():
+    case = _case("tiny")
+    S = 4
+    out = torch.empty_like(case.q)
+    ws = torch.empty(pfkv.workspace_bytes(S, case.q.shape[0], case.q.shape[1]), dtype=torch.uint8, device=DEV)
+    eager = run(case, num_segments=S).clone()
+    stream = torch.cuda.Stream()
+    run(case, num_segments=S, out=out, workspace=ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run(case, num_segments=S, out=out, workspace=ws)
+    for k in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {k} differs"
+        other = run(case, num_segments=S)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
+
+
+def test_page_permutation_bitwise():
+    case = _case("multigroup")
+    shuffled = permute_pool(case, seed=123)
+    a = run(case, num_segments=5)
+    b = run(shuffled, num_segments=5)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_rerun_bitwise():
+    case = _case("ragged")
+    a = run(case)
+    outs = [run(case) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(a.view(torch.int16), o.view(torch.int16))
+
+
+@pytest.mark.parametrize("group", [16, 8])
+def test_short_qlen_rows_match_verify_bitwise(group):
+    """Draft-extend (q_len 1..3) and decode rows equal the verify call's rows bit for bit."""
+    w = Workload(name="v", ctx=(5000, 777, 40, 16), q_lens=(4, 4, 4, 4), num_q_heads=group, num_kv_heads=1,
+                 num_segments=8, seed=34)
+    case = make_case(w, "cpu").to(DEV)
+    verify = run(case, num_segments=8)
+    for q_len in (1, 2, 3):
+        rows = [4 * b + 4 - q_len + i for b in range(w.num_seqs) for i in range(q_len)]
+        q = case.q[torch.tensor(rows, device=DEV)].contiguous()
+        cu = torch.arange(0, q_len * (w.num_seqs + 1), q_len, dtype=torch.int32, device=DEV)
+        short = pfkv.verify_attn(q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, cu,
+                                 case.k_descale, case.v_descale, case.softmax_scale, num_segments=8)
+        torch.cuda.synchronize()
+        assert torch.equal(short.view(torch.int16), verify[torch.tensor(rows, device=DEV)].view(torch.int16)), q_len
+
+
+# ------------------------------------------------------------------ closed forms and edge cases
+def _one_sequence(k_codes, v_codes, q, q_len, kd=1.0, vd=1.0, scale=1.0 / 16, hkv=1):
+    """Device Case for one sequence with hand-set fp8 codes ([L, Hkv, 256]) and Q values."""
+    L = k_codes.shape[0]
+    n_pages = -(-L // 16)
+    kc = torch.zeros((n_pages + 1, 16, hkv, 256), dtype=torch.uint8)
+    vc = torch.zeros_like(kc)
+    kc.view(-1, hkv, 256)[:L] = torch.from_numpy(k_codes)
+    vc.view(-1, hkv, 256)[:L] = torch.from_numpy(v_codes)
+    kc[n_pages] = 0x7F
+    vc[n_pages] = 0x7F
+    table = torch.arange(n_pages, dtype=torch.int32)[None]
+    w = Workload(name="h", ctx=(L,), q_lens=(q_len,), num_q_heads=q.shape[1], num_kv_heads=hkv, num_segments=1,
+                 seed=0)
+    case = Case(torch.from_numpy(q).to(torch.bfloat16), kc, vc, table, torch.tensor([L], dtype=torch.int32),
+                torch.tensor([0, q_len], dtype=torch.int32), torch.tensor([kd], dtype=torch.float32),
+                torch.tensor([vd], dtype=torch.float32), scale, n_pages, w)
+    return case.to(DEV)
+
+
+def _code(value):
+    table = oracle.e4m3fn_decode_table()
+    return int(np.flatnonzero(table == value)[0])
+
+
+def test_dominant_key_keeps_small_probabilities():
+    # one key with score 7, the other 3999 keys score 0; V = +1 on key 0, -1 elsewhere
+    n = 4000
+    k = np.zeros((n, 1, 256), np.uint8)
+    k[0, 0, 0] = _code(14.0)
+    v = np.full((n, 1, 256), _code(-1.0), np.uint8)
+    v[0] = _code(1.0)
+    q = np.zeros((1, 16, 256), np.float32)
+    q[0, :, 0] = 8.0
+    case = _one_sequence(k, v, q, 1)
+    exact = (math.exp(7.0) - (n - 1)) / (math.exp(7.0) + (n - 1))
+    ref = oracle_for(case)
+    assert abs(ref[0, 0, 0] - exact) < 1e-12
+    for segments in (1, 4, 16):
+        out = run(case, num_segments=segments)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        print(f"[dominant] S={segments} got {got[0, 0, 0]:.5f} exact {exact:.5f}", flush=True)
+        assert np.max(np.abs(got - exact)) < 1e-2
+
+
+def test_single_key_returns_v_exactly():
+    rng = np.random.default_rng(7)
+    finite = np.flatnonzero(~np.isnan(oracle.e4m3fn_decode_table()))
+    k = rng.choice(finite, size=(1, 1, 256)).astype(np.uint8)
+    v = rng.choice(finite, size=(1, 1, 256)).astype(np.uint8)
+    q = rng.standard_normal((1, 16, 256)).astype(np.float32)
+    case = _one_sequence(k, v, q, 1, kd=0.37, vd=0.25)
+    out = run(case, num_segments=1)
+    torch.cuda.synchronize()
+    expect = torch.from_numpy(oracle.e4m3fn_decode_table()[v[0, 0]] * 0.25).to(torch.bfloat16)
+    assert torch.equal(out[0].cpu().view(torch.int16), expect[None].expand(16, 256).view(torch.int16))
+
+
+def test_identical_keys_give_prefix_means():
+    rng = np.random.default_rng(8)
+    table = oracle.e4m3fn_decode_table()
+    small = np.flatnonzero(np.abs(table) < 4)
+    L = 333
+    k = np.repeat(rng.choice(small, size=(1, 1, 256)).astype(np.uint8), L, axis=0)
+    v = rng.choice(small, size=(L, 1, 256)).astype(np.uint8)
+    q = rng.standard_normal((4, 16, 256)).astype(np.float32)
+    case = _one_sequence(k, v, q, 4)
+    out = run(case, num_segments=3).float().cpu().numpy()
+    vals = table[v[:, 0, :]]
+    for i in range(4):
+        mean = vals[: L - 4 + i + 1].mean(axis=0)
+        assert np.max(np.abs(out[i] - mean[None])) < 4e-3
+
+
+def test_zero_length_query_sequences():
+    w = Workload(name="z", ctx=(100, 50, 80, 2000), q_lens=(4, 0, 2, 0), num_q_heads=16, num_kv_heads=1,
+                 num_segments=4, seed=35)
+    case = make_case(w, "cpu").to(DEV)
+    out = run(case, num_segments=4)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), "zero q_len entries")
+
+
+def test_strided_q_and_out():
+    case = _case("multigroup")
+    T, Hq, D = case.q.shape
+    big_q = torch.zeros((T, Hq + 3, D + 64), dtype=torch.bfloat16, device=DEV)
+    big_q[:, :Hq, :D] = case.q
+    q_view = big_q[:, :Hq, :D]
+    big_out = torch.zeros((T, Hq + 1, D + 32), dtype=torch.bfloat16, device=DEV)
+    out_view = big_out[:, :Hq, :D]
+    ref = run(case, num_segments=6)
+    pfkv.verify_attn(q_view, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.cu_seqlens_q,
+                     case.k_descale, case.v_descale, case.softmax_scale, num_segments=6, out=out_view)
+    torch.cuda.synchronize()
+    assert torch.equal(out_view.contiguous().view(torch.int16), ref.view(torch.int16))
+    assert torch.all(big_out[:, Hq:, :] == 0) and torch.all(big_out[:, :, D:] == 0)
+
+
+def test_unsupported_group_is_refused():
+    w = Workload(name="u", ctx=(64,), q_lens=(4,), num_q_heads=4, num_kv_heads=1, num_segments=1, seed=1)
+    case = make_case(w, "cpu").to(DEV)
+    with pytest.raises(pfkv.PfkvError) as info:
+        run(case, num_segments=1)
+    assert info.value.status == 2
+
+
+def test_host_pointer_is_refused():
+    case = _case("tiny")
+    with pytest.raises(ValueError):
+        pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables.cpu(), case.seq_lens,
+                         case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, num_segments=4)
+
+
+def test_stream_read_variants_run():
+    buf = torch.ones(64 << 20, dtype=torch.uint8, device=DEV)
+    order = torch.randperm((64 << 20) // 4096, device=DEV).to(torch.int32)
+    for variant in (0, 1, 2):
+        pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None)
+    torch.cuda.synchronize()

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, validation, heuristics."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_fp8_kv_split_amd as pfkv
+from paged_fp8_kv_split_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pfkv.library_path()):
+        from paged_fp8_kv_split_amd.build import build
+        build()
+    return pfkv.load_library()
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pfkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pfkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_symbols()
+    assert "pfkv_verify_attn_fwd" in names and len(names) >= 7
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    # pointers (10 x 8) + int64/uint64 (6 x 8) + 9 int32 + 1 float
+    assert ctypes.sizeof(binding.PfkvArgs) == 10 * 8 + 6 * 8 + 10 * 4
+
+
+def _valid_args(**over):
+    a = binding.PfkvArgs()
+    base = 0x100000
+    for k, name in enumerate(["q", "k_cache", "v_cache", "block_tables", "seq_lens", "cu_seqlens_q",
+                              "k_descale", "v_descale", "workspace", "out"]):
+        setattr(a, name, base + 0x10000 * k)
+    a.q_stride_token, a.q_stride_head = 16 * 256, 256
+    a.out_stride_token, a.out_stride_head = 16 * 256, 256
+    a.block_table_stride = 2200
+    a.num_seqs, a.total_q, a.num_q_heads, a.num_kv_heads = 16, 64, 16, 1
+    a.head_dim, a.page_size, a.num_pages, a.max_pages_per_seq = 256, 16, 70000, 2188
+    a.num_segments = 16
+    a.softmax_scale = 1.0 / 16
+    a.workspace_size = pfkv.workspace_bytes(16, 64, 16)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+CASES = [
+    ("valid", {}, "gfx950:sramecc+:xnack-", OK),
+    ("bare arch name", {}, "gfx950", OK),
+    ("gqa8", dict(num_q_heads=8, q_stride_token=8 * 256, out_stride_token=8 * 256,
+                  workspace_size=pfkv.workspace_bytes(16, 64, 8)), "gfx950", OK),
+    ("two kv heads", dict(num_q_heads=32, num_kv_heads=2, workspace_size=pfkv.workspace_bytes(16, 64, 32)),
+     "gfx950", OK),
+    ("null q", dict(q=0), "gfx950", INVALID),
+    ("null out", dict(out=0), "gfx950", INVALID),
+    ("null descale", dict(v_descale=0), "gfx950", INVALID),
+    ("zero seqs", dict(num_seqs=0), "gfx950", INVALID),
+    ("too many queries", dict(total_q=65), "gfx950", INVALID),
+    ("heads not divisible", dict(num_q_heads=15, num_kv_heads=2), "gfx950", INVALID),
+    ("zero kv heads", dict(num_kv_heads=0), "gfx950", INVALID),
+    ("segments 0", dict(num_segments=0), "gfx950", INVALID),
+    ("segments 65", dict(num_segments=65), "gfx950", INVALID),
+    ("workspace too small", dict(workspace_size=pfkv.workspace_bytes(16, 64, 16) - 1), "gfx950", INVALID),
+    ("nan scale", dict(softmax_scale=float("nan")), "gfx950", INVALID),
+    ("inf scale", dict(softmax_scale=float("inf")), "gfx950", INVALID),
+    ("negative scale", dict(softmax_scale=-0.0625), "gfx950", INVALID),
+    ("table stride", dict(block_table_stride=100), "gfx950", INVALID),
+    ("q stride odd", dict(q_stride_head=255), "gfx950", INVALID),
+    ("q misaligned", dict(q=0x100008), "gfx950", INVALID),
+    ("out stride", dict(out_stride_head=2), "gfx950", INVALID),
+    ("workspace misaligned", dict(workspace=0x180004), "gfx950", INVALID),
+    ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
+    ("page 32", dict(page_size=32), "gfx950", UNSUPPORTED),
+    ("gqa 4", dict(num_q_heads=4, workspace_size=pfkv.workspace_bytes(16, 64, 4)), "gfx950", UNSUPPORTED),
+    ("gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32)), "gfx950", UNSUPPORTED),
+    ("mi300", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
+    ("gfx9500 lookalike", {}, "gfx9500", UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,over,arch,expect", CASES, ids=[c[0] for c in CASES])
+def test_check_args_table(lib, name, over, arch, expect):
+    a = _valid_args(**over)
+    status = binding.check_args(a, arch)
+    assert status == expect, (name, status, binding.last_error())
+    if expect != OK:
+        assert binding.last_error()
+
+
+def test_check_args_rejects_bad_host_inputs(lib):
+    assert lib.pfkv_check_args(None, b"gfx950", 256) == INVALID
+    a = _valid_args()
+    assert lib.pfkv_check_args(ctypes.byref(a), None, 256) == INVALID
+    assert lib.pfkv_check_args(ctypes.byref(a), b"gfx950", 0) == INVALID
+
+
+@pytest.mark.parametrize("cus,n,hkv,expect", [
+    (256, 16, 1, 16), (256, 4, 1, 64), (256, 8, 1, 32), (256, 2, 2, 64), (256, 1, 1, 64),
+    (256, 300, 1, 1), (256, 256, 1, 1), (256, 128, 1, 2), (304, 16, 1, 19), (0, 16, 1, 0), (256, 0, 1, 0),
+])
+def test_num_segments_heuristic(lib, cus, n, hkv, expect):
+    assert pfkv.num_segments(cus, n, hkv) == expect
+
+
+def test_workspace_bytes(lib):
+    assert pfkv.workspace_bytes(16, 64, 16) == 16 * 64 * 16 * 258 * 4
+    assert pfkv.workspace_bytes(0, 64, 16) == 0
+    assert pfkv.workspace_bytes(64, 8, 32) == 64 * 8 * 32 * 258 * 4
+
+
+def test_stream_read_validation(lib):
+    assert lib.pfkv_stream_read(None, 4096, 0, None, 0, None, None) == INVALID
+    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, 3, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 100, 1, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, 2, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+
+
+def test_python_wrapper_needs_gpu_tensors():
+    import torch
+    q = torch.zeros(4, 16, 256, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        pfkv.verify_attn(q, None, None, None, None, None, None, None, 0.0625)
+
+
+def test_ragged_workload_is_seeded_and_in_range():
+    from paged_fp8_kv_split_amd.workloads import workload
+    w = workload("ragged")
+    assert w.num_seqs == 8 and all(1 <= q <= 4 for q in w.q_lens)
+    assert all(6 <= c <= 105000 and c >= q for c, q in zip(w.ctx, w.q_lens))
+    assert w == workload("ragged")
