@@ -7,15 +7,20 @@
 // device pointers. In-kernel q_len 1..4 follows SGLang PR #37465, Modifications.
 // The decomposition is this library's own:
 //
-// * 4 waves per work-group, one per SIMD. A step covers 4 pages (64 keys): wave
-//   w streams page w of the step HBM -> LDS and computes its 16 keys' scores
-//   against all G * q_len (<= 64) stacked query rows; for P V every wave covers
-//   all 64 keys but only its own 64 of the 256 output dims, so the fp32
-//   accumulator is 64 registers per lane and no work is duplicated.
+// * 8 waves per work-group, two per SIMD. A step covers 4 pages (64 keys).
+//   Page slot j of the step belongs to the wave pair (j, j + 4): the pair streams
+//   it HBM -> LDS (one wave K, the other V) and computes its 16 keys' scores,
+//   each wave for half of the G * q_len (<= 64) stacked query rows. For P V every
+//   wave covers all 64 keys but only 32 of the 256 output dims, so the fp32
+//   accumulator is 32 registers per lane and P V is never duplicated.
+// * Q is loaded once into registers in the MFMA operand layout.
 // * K/V pages move with global_load_lds_dwordx4 (1 KiB contiguous per
 //   instruction) issued from inline asm, so the compiler does not serialise LDS
-//   reads behind every outstanding transfer; a 3-stage ring keeps two steps
-//   (64 KiB per work-group) in flight, with explicit vmcnt waits.
+//   reads behind every outstanding transfer; a 4-stage ring keeps the next two
+//   steps (64 KiB) in flight while one is consumed, with explicit vmcnt waits.
+// * One work-group barrier per step. Between barriers t and t+1 each wave does
+//   P V of step t and the scores of step t+1 (independent MFMA chains), then the
+//   softmax of step t+1.
 // * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K converts exactly from e4m3fn to
 //   bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), Q stays bf16. The score layout
 //   puts one query row per lane column: row maxima need one in-lane reduction and
@@ -23,14 +28,16 @@
 // * Online softmax in the log2 domain with a lazy reference max m per row: m
 //   moves only when a row's running max exceeds it by more than 8, so
 //   P = 2^(s - m) <= 2^8 fits fp16 and the accumulator is rescaled rarely. Each
-//   wave computes P against the current m and publishes it with its local row
-//   maxima; one barrier per step. If any wave saw a row exceed m + 8, all waves
-//   take the (rare) slow path: new m from the step's maxima, rescale, recompute
-//   P, second barrier. Rows that did not need it keep m and get bit-identical P,
-//   so each row's arithmetic depends only on that row.
+//   wave computes P against the current m and publishes it with its row maxima.
+//   If any wave saw a row exceed m + 8, all waves take the (rare) slow path: new
+//   m from the step's maxima, rescale, recompute P, one more barrier. Rows that
+//   did not need it keep m and get bit-identical P, so each row's arithmetic
+//   depends only on that row.
 // * P is rounded to fp16 once; the same values feed the row sum l and P V.
 // * O += P V on v_mfma_f32_16x16x32_f16. V's transposed operand comes from
 //   ds_read_b64_tr_b8 and converts exactly to fp16.
+#include <type_traits>
+
 #include "pfkv_internal.h"
 
 namespace pfkv {
@@ -43,35 +50,35 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 typedef __attribute__((address_space(4))) const float const_f32;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPagesPerStep = kWaves;                  // one page per wave per step
-constexpr int kStages = 3;                             // LDS ring depth
+constexpr int kPagesPerStep = 4;                       // one page per wave pair
+constexpr int kStages = 4;                             // LDS ring depth (steps)
 constexpr int kPageBytes = kPageSize * kHeadDim;       // one (page, head) block of K or V: 4 KiB
-constexpr int kStageBytes = 2 * kPagesPerStep * kPageBytes;   // K and V of the step: 32 KiB
-constexpr int kDmaPerPage = 2 * kPageBytes / 1024;     // 8 x 1 KiB (K and V)
-constexpr int kDimsPerWave = kHeadDim / kWaves;        // 64
+constexpr int kStageBytes = 2 * kPagesPerStep * kPageBytes;   // K and V of one step: 32 KiB
+constexpr int kDmaPerWave = kPageBytes / 1024;         // 4 x 1 KiB per wave per step
+constexpr int kDimsPerWave = kHeadDim / kWaves;        // 32
 constexpr float kLazySlack = 8.0f;                     // log2 units
 
 template <int G>
 struct Cfg {
-  static constexpr int kRowBlocks = G * kMaxQLen / 16;            // 16-row MFMA blocks
+  static constexpr int kRowBlocks = G * kMaxQLen / 16;            // 16-row MFMA blocks (all rows)
+  static constexpr int kHalfBlocks = kRowBlocks / 2;               // row blocks scored by one wave
   static constexpr int kRows = kRowBlocks * 16;
-  static constexpr int kQBytes = kRows * kHeadDim * 2;             // bf16 Q rows
-  static constexpr int kPBytes = kRowBlocks * kWaves * 64 * 8;     // fp16 P of one step
-  static constexpr int kMxBytes = kWaves * kRows * 4;              // per-wave row maxima of one step
-  static constexpr int kOffP = kQBytes;                            // two P buffers
+  static constexpr int kPBytes = kRowBlocks * kPagesPerStep * 64 * 8;   // fp16 P of one step
+  static constexpr int kMxBytes = kPagesPerStep * kRows * 4;       // per-page row maxima of one step
+  static constexpr int kOffP = 0;                                  // two P buffers
   static constexpr int kOffMx = kOffP + 2 * kPBytes;               // two maxima buffers
   static constexpr int kOffFlag = kOffMx + 2 * kMxBytes;           // two flag words per wave
   static constexpr int kOffStage = kOffFlag + 64;
   static constexpr int kLdsBytes = kOffStage + kStages * kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kPagesPerStep * kRows * 4 + kRows * 4 <= kLdsBytes, "epilogue scratch");
 };
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -94,10 +101,13 @@ __device__ __forceinline__ void dma_1k(const uint8_t* sbase, unsigned voff, unsi
 }
 
 // Wait until at most `pending` of this wave's vector-memory operations are in
-// flight. Inside the main loop the only such operations are the page transfers.
+// flight (0, 4 or 8). Inside the main loop the only such operations are the
+// page transfers.
 __device__ __forceinline__ void wait_vm(int pending) {
   if (pending >= 8)
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (pending >= 4)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -126,46 +136,39 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(unsigned lo, unsigned hi) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int G>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-splitkv_main_kernel(MainParams p) {
-  using C = Cfg<G>;
-  constexpr int RB = C::kRowBlocks;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
+// Geometry of one work-group's (segment, sequence, KV head), uniform.
+struct Geo {
+  int seg, b, h;
+  int q0, q_len, L, pb, pe, rows, n_steps;
+  float c2;          // k_descale * softmax_scale * log2(e)
+};
 
-  const int seg = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+// The work of one work-group, specialised on the number NRB of 16-row blocks
+// that hold real query rows (G * q_len rows), so that the steady-state loop is
+// straight-line code.
+template <int G, int NRB>
+__device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
+  using C = Cfg<G>;
+  constexpr int JMAX = (NRB + 1) / 2;            // row blocks scored per wave: hf + 2 j
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = w & 3;          // page slot scored by this wave
+  const int hf = w >> 2;         // which interleaved half of the row blocks it scores
   const int lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int h = geo.h, q0 = geo.q0, q_len = geo.q_len, L = geo.L, pb = geo.pb, pe = geo.pe;
+  const int rows = geo.rows, n_steps = geo.n_steps;
+  // with an even NRB both halves score JMAX blocks; with an odd one half scores fewer
+  auto scored = [&](int j) -> bool { return (NRB % 2 == 0) || (hf + 2 * j < NRB); };
 
-  const const_i32* cu = (const const_i32*)p.cu_seqlens_q;
-  const const_i32* sl = (const const_i32*)p.seq_lens;
   const const_i32* bt = (const const_i32*)p.block_tables;
-
-  // ---- sequence geometry (uniform); out-of-contract values are clamped so that
-  // every access stays inside its buffer.
-  const int q0 = cu[b];
-  int q_len = cu[b + 1] - q0;
-  if (q0 < 0 || q0 >= p.total_q) q_len = 0;
-  q_len = min(max(q_len, 0), min(kMaxQLen, p.total_q - max(q0, 0)));
-  if (q_len <= 0) return;
-  const int L = min(max(sl[b], 0), p.max_pages_per_seq * kPageSize);
-  const int pages = (L + kPageSize - 1) / kPageSize;
-  const int chunk = (pages + p.num_segments - 1) / p.num_segments;
-  const int pb = min(seg * chunk, pages);
-  const int pe = min(pb + chunk, pages);
-  const int rows = G * q_len;
-  const int n_steps = (pe - pb + kPagesPerStep - 1) / kPagesPerStep;
-  const float c2 = *(const const_f32*)p.k_descale * p.score_scale_log2;
-
-  const int64_t bt_row = (int64_t)b * p.block_table_stride;
+  const int64_t bt_row = (int64_t)geo.b * p.block_table_stride;
   const uint64_t page_stride = (uint64_t)kPageSize * p.num_kv_heads * kHeadDim;
 
   // ---- per-lane DMA offsets inside one (page, head) block. In LDS, the
   // 16-byte chunk at position pos of key row k (page slot j) holds dim chunk
   // pos ^ sw(k, j), sw(k, j) = (k ^ 12 (j & 1)) & 15: K row reads and V
   // transposed reads are then free of bank conflicts.
-  const int jpar = w & 1;
+  const int jpar = pw & 1;
   unsigned goff[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -175,60 +178,61 @@ splitkv_main_kernel(MainParams p) {
   uint8_t* const stage0 = smem + C::kOffStage;
   const unsigned stage0_lds = lds_addr(stage0);
 
+  // wave (pw, 0) moves K of page slot pw, wave (pw, 1) moves V
+  auto has_page = [&](int t) -> bool { return t < n_steps && pb + kPagesPerStep * t + pw < pe; };
   auto issue_step = [&](int t) {
-    const int pidx = pb + kPagesPerStep * t + w;
-    if (pidx < pe) {
-      int id = bt[bt_row + pidx];
+    if (has_page(t)) {
+      int id = bt[bt_row + pb + kPagesPerStep * t + pw];
       id = min(max(id, 0), p.num_pages - 1);
-      const uint8_t* kbase = p.k_cache + (uint64_t)id * page_stride;
-      const uint8_t* vbase = p.v_cache + (uint64_t)id * page_stride;
-      const unsigned dst = stage0_lds + (t % kStages) * kStageBytes + w * kPageBytes;
+      const uint8_t* base = (hf == 0 ? p.k_cache : p.v_cache) + (uint64_t)id * page_stride;
+      const unsigned dst = stage0_lds + (t % kStages) * kStageBytes + hf * kPagesPerStep * kPageBytes +
+                           pw * kPageBytes;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        dma_1k(kbase, goff[jj], dst + 1024 * jj);
-        dma_1k(vbase, goff[jj], dst + kPagesPerStep * kPageBytes + 1024 * jj);
-      }
+      for (int jj = 0; jj < 4; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
     }
   };
-  auto has_page = [&](int t) -> bool { return t < n_steps && pb + kPagesPerStep * t + w < pe; };
+  auto dma_count = [&](int t) -> int { return has_page(t) ? kDmaPerWave : 0; };
 
-  // ---- prologue: two steps in flight, then stage Q while they land.
+  // ---- prologue: step 0's pages and Q fly together; steps 1 and 2 follow.
   issue_step(0);
-  if (n_steps > 1) issue_step(1);
 
-  // Q rows r = i * G + gg (query i of the sequence, head h * G + gg); row r's
-  // 16-byte chunk c16 sits at position c16 ^ (r & 15).
-  // All loads are issued before any LDS write so their latencies overlap.
-  constexpr int kQChunks = C::kRows * 32 / kThreads;
-  u32x4 qv[kQChunks];
+  // Q^T operand of the score MFMA for rows 16 (hf + 2 j) + n: k-slots 8g..8g+7
+  // of k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8.
+  bf16x8 qop[JMAX][4][2];
 #pragma unroll
-  for (int c = 0; c < kQChunks; ++c) {
-    const int idx = tid + c * kThreads;
-    const int r = idx >> 5, c16 = idx & 31;
-    // padding rows load row 0 (always valid) and are zeroed below: no branch
-    const int rr = r < rows ? r : 0;
+  for (int j = 0; j < JMAX; ++j) {
+    const int r = 16 * (hf + 2 * j) + n;
+    const int rr = r < rows ? r : 0;                 // padding rows read row 0, zeroed below
     const int i = rr / G, gg = rr - (rr / G) * G;
     const uint16_t* src = p.q + (int64_t)(q0 + i) * p.q_stride_token + (int64_t)(h * G + gg) * p.q_stride_head;
-    qv[c] = *(const u32x4*)(src + 8 * c16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) qop[j][u][hh] = *(const bf16x8*)(src + 16 * (4 * u + g) + 8 * hh);
   }
 #pragma unroll
-  for (int c = 0; c < kQChunks; ++c) {
-    const int r = (tid + c * kThreads) >> 5;
-    if (r >= rows) qv[c] = u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int j = 0; j < JMAX; ++j) {
+    const bool pad = 16 * (hf + 2 * j) + n >= rows;
 #pragma unroll
-  for (int c = 0; c < kQChunks; ++c) {
-    const int idx = tid + c * kThreads;
-    const int r = idx >> 5, c16 = idx & 31;
-    *(u32x4*)(smem + r * 512 + 16 * (c16 ^ (r & 15))) = qv[c];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) qop[j][u][hh] = pad ? bf16x8{} : qop[j][u][hh];
   }
-  __syncthreads();
+  // The compiler waits for the Q loads before these statements (they read
+  // qop); step 0's transfers, issued earlier, have then landed as well.
+  // Issuing steps 1 and 2 only afterwards keeps the compiler's own waits on Q
+  // from draining them.
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) asm volatile("" : "+v"(qop[j][u][hh]) :: "memory");
+  issue_step(1);
+  issue_step(2);
 
   // ---- per-lane LDS read offsets
   const unsigned kcol = 16u * ((g ^ n ^ (12 * jpar)) & 15);
-  unsigned qcol[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) qcol[hh] = 16u * ((2 * g + hh) ^ n);
   // V^T operand: source lane n of group g supplies the 8 dims at +8 (n & 1) of
   // key 4g + ((n >> 1) & 3) in page slot 2 ks + (n >> 3), the k-slot (n >> 1)
   // of group g; ds_read_b64_tr_b8 hands lane n byte k of source lane 2k + n/8.
@@ -237,178 +241,227 @@ splitkv_main_kernel(MainParams p) {
   const unsigned vrow = (unsigned)(kPagesPerStep * kPageBytes + vpar * kPageBytes + 256 * vkey + 8 * (n & 1));
   const unsigned vsw = 16u * ((vkey ^ (12 * vpar)) & 15);
 
-  f32x4 acc[RB][4];
-  float m_ref[RB], l_lane[RB];
+  // Scores of this wave's page of step t for its row blocks: lane (g, n) holds
+  // key 4g + r of the page against row 16 (hf + 2 j) + n, in log2 units. In tail
+  // steps the page may be missing and keys past a row's causal limit (or the
+  // sequence end) are masked to -inf; steady-state steps need neither.
+  auto score_step = [&](int t, float (&sv)[JMAX][4], auto tail) {
+    constexpr bool kTail = decltype(tail)::value;
+    const int pidx = pb + kPagesPerStep * t + pw;
+    if (!kTail || has_page(t)) {
+      const uint8_t* kp = stage0 + (t % kStages) * kStageBytes + pw * kPageBytes + 256 * n;
+      f32x4 sacc[JMAX];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_ref[rb] = -__builtin_inff();
-    l_lane[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int t = 0; t < n_steps; ++t) {
-    const int st = t % kStages, buf = t & 1;
-    const uint8_t* sp = stage0 + st * kStageBytes;
-    const int pidx = pb + kPagesPerStep * t + w;        // this wave's page
-    const bool mine = pidx < pe;
-    wait_vm(has_page(t + 1) ? kDmaPerPage : 0);
-
-    // ---- S^T[key][row] = K Q^T for this wave's page (k-slots permuted consistently)
-    float sv[RB][4];
-    if (mine) {
-      f32x4 sacc[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < JMAX; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 raw = *(const u32x4*)(sp + w * kPageBytes + 256 * n + (kcol ^ (64u * u)));
+        const u32x4 raw = *(const u32x4*)(kp + (kcol ^ (64u * u)));
         const bf16x8 k0 = fp8x8_to_bf16(raw[0], raw[1]);
         const bf16x8 k1 = fp8x8_to_bf16(raw[2], raw[3]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint8_t* qrow = smem + 8192 * rb + 512 * n;
-          const bf16x8 qa = *(const bf16x8*)(qrow + (qcol[0] ^ (128u * u)));
-          const bf16x8 qb = *(const bf16x8*)(qrow + (qcol[1] ^ (128u * u)));
-          sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qa, sacc[rb], 0, 0, 0);
-          sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb, sacc[rb], 0, 0, 0);
+        for (int j = 0; j < JMAX; ++j) {
+          if (scored(j)) {
+            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[j][u][0], sacc[j], 0, 0, 0);
+            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[j][u][1], sacc[j], 0, 0, 0);
+          }
         }
       }
-      // scale to log2 units; mask keys past the row's causal limit or the sequence
-      const bool need_mask = kPageSize * (pidx + 1) > L - q_len + 1;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = (16 * rb + n) / G;
+      for (int j = 0; j < JMAX; ++j) {
+        const int i = (16 * (hf + 2 * j) + n) / G;
         const int lim = min(L - 1, L - q_len + i);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float s = sacc[rb][r] * c2;
-          const int key = kPageSize * pidx + 4 * g + r;
-          sv[rb][r] = (!need_mask || key <= lim) ? s : -__builtin_inff();
+          const float s = sacc[j][r] * geo.c2;
+          if constexpr (kTail) {
+            const int key = kPageSize * pidx + 4 * g + r;
+            sv[j][r] = key <= lim ? s : -__builtin_inff();
+          } else {
+            sv[j][r] = s;
+          }
         }
       }
     } else {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int j = 0; j < JMAX; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[rb][r] = -__builtin_inff();
+        for (int r = 0; r < 4; ++r) sv[j][r] = -__builtin_inff();
     }
+  };
 
-    // ---- local row maxima, slow-path flag, P against the current reference
+  f32x4 acc[NRB][2];
+  float m_ref[NRB];         // reference max of row 16 rb + n, identical in every wave
+  float l_lane[JMAX];       // this lane's share of the row sums of its scored rows
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    m_ref[rb] = -__builtin_inff();
+    acc[rb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) l_lane[j] = 0.f;
+
+  // step 0 has landed in every wave (steps 1 and 2 may still fly): score it
+  lds_barrier();
+  float sv[JMAX][4];
+  if (n_steps > 3)
+    score_step(0, sv, std::false_type{});
+  else
+    score_step(0, sv, std::true_type{});
+
+  // One step: softmax of step t, barrier, P V of step t and the scores of
+  // step t+1. Steady-state steps (t + 3 < n_steps) have all pages of steps t,
+  // t+1, t+2 present and no masking.
+  auto step = [&](int t, auto tail) {
+    constexpr bool kTail = decltype(tail)::value;
+    const int buf = t & 1;
     float* mx_buf = (float*)(smem + C::kOffMx + buf * C::kMxBytes);
     int* flags = (int*)(smem + C::kOffFlag) + buf * kWaves;
     uint8_t* p_buf = smem + C::kOffP + buf * C::kPBytes;
+
+    // ---- softmax of step t: local row maxima, slow-path flag, P vs current m
     bool over = false;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      over |= mx > m_ref[rb] + kLazySlack;
-      if (g == 0) mx_buf[w * C::kRows + 16 * rb + n] = mx;
+    for (int j = 0; j < JMAX; ++j) {
+      if (scored(j)) {
+        const int rb = hf + 2 * j;
+        float mx = fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        over |= mx > m_ref[rb] + kLazySlack;
+        if (g == 0) mx_buf[pw * C::kRows + 16 * rb + n] = mx;
+      }
     }
     const bool wave_over = __any(over);
     if (lane == 0) flags[w] = wave_over ? 1 : 0;
-
-    f16x4 pv[RB];
+    f16x4 pv[JMAX];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[rb][r] = (_Float16)__builtin_amdgcn_exp2f(sv[rb][r] - mref);
-      *(f16x4*)(p_buf + ((rb * kWaves + w) * 64 + lane) * 8) = pv[rb];
-    }
-    lds_barrier();
-
-    if (flags[0] | flags[1] | flags[2] | flags[3]) {
-      // slow path (uniform over the work-group): move m where a row's step max
-      // exceeds it by more than the slack, rescale, recompute and republish P
-      float alpha[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float M = mx_buf[0 * C::kRows + 16 * rb + n];
-#pragma unroll
-        for (int v = 1; v < kWaves; ++v) M = fmaxf(M, mx_buf[v * C::kRows + 16 * rb + n]);
-        alpha[rb] = 1.f;
-        if (M > m_ref[rb] + kLazySlack) {
-          alpha[rb] = __builtin_amdgcn_exp2f(m_ref[rb] - M);   // 0 when m was -inf
-          m_ref[rb] = M;
-        }
-        l_lane[rb] *= alpha[rb];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = __shfl(alpha[rb], 4 * g + r, 64);   // lane 4g+r holds row 4g+r
-#pragma unroll
-          for (int db = 0; db < 4; ++db) acc[rb][db][r] *= a;
-        }
+    for (int j = 0; j < JMAX; ++j) {
+      if (scored(j)) {
+        const int rb = hf + 2 * j;
         const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[rb][r] = (_Float16)__builtin_amdgcn_exp2f(sv[rb][r] - mref);
+        for (int r = 0; r < 4; ++r) pv[j][r] = (_Float16)__builtin_amdgcn_exp2f(sv[j][r] - mref);
+        *(f16x4*)(p_buf + ((rb * kPagesPerStep + pw) * 64 + lane) * 8) = pv[j];
       }
-      // nobody reads this step's P before the barrier below
+    }
+
+    // step t+1's pages must have landed (step t+2's may still fly)
+    if constexpr (kTail)
+      wait_vm(dma_count(t + 2));
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lds_barrier();
+
+    bool any_flag = false;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) *(f16x4*)(p_buf + ((rb * kWaves + w) * 64 + lane) * 8) = pv[rb];
+    for (int v = 0; v < kWaves; ++v) any_flag |= flags[v] != 0;
+    if (any_flag) {
+      // slow path (uniform over the work-group): move m where a row's step max
+      // exceeds it by more than the slack; rescale; recompute and republish P
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float M = mx_buf[0 * C::kRows + 16 * rb + n];
+#pragma unroll
+        for (int v = 1; v < kPagesPerStep; ++v) M = fmaxf(M, mx_buf[v * C::kRows + 16 * rb + n]);
+        float alpha = 1.f;
+        if (M > m_ref[rb] + kLazySlack) {
+          alpha = __builtin_amdgcn_exp2f(m_ref[rb] - M);   // 0 when m was -inf
+          m_ref[rb] = M;
+        }
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j)
+          if (scored(j) && rb == hf + 2 * j) l_lane[j] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = __shfl(alpha, 4 * g + r, 64);     // lane 4g+r holds row 4g+r
+          acc[rb][0][r] *= a;
+          acc[rb][1][r] *= a;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) {
+        if (scored(j)) {
+          const int rb = hf + 2 * j;
+          const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[j][r] = (_Float16)__builtin_amdgcn_exp2f(sv[j][r] - mref);
+          *(f16x4*)(p_buf + ((rb * kPagesPerStep + pw) * 64 + lane) * 8) = pv[j];
+        }
+      }
       lds_barrier();
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      l_lane[rb] += ((float)pv[rb][0] + (float)pv[rb][1]) + ((float)pv[rb][2] + (float)pv[rb][3]);
+    for (int j = 0; j < JMAX; ++j)
+      if (scored(j)) l_lane[j] += ((float)pv[j][0] + (float)pv[j][1]) + ((float)pv[j][2] + (float)pv[j][3]);
 
-    // every wave is past step t-1: its stage can take step t+2
-    if (t + 2 < n_steps) issue_step(t + 2);
+    // every wave is past step t-1: its stage takes step t+3
+    issue_step(t + 3);
 
-    // ---- O[:, own dims] += P V over the step's 64 keys (two k-steps of 32).
+    // ---- O[:, own dims] += P V over step t's 64 keys (two k-steps of 32).
     // k-slot 8g + e of k-step ks is key 4g + (e & 3) of page slot 2 ks + (e >> 2).
-    // keys of pages past the segment (never loaded: stale or uninitialised LDS)
-    // and past the sequence end get V = 0, so that P = 0 never meets a NaN
-    const int step_end = pb + kPagesPerStep * (t + 1);
-    const bool mask_v = step_end > pe || kPageSize * step_end > L;
+    const uint8_t* sp = stage0 + (t % kStages) * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      f16x8 pa[RB];
+      f16x8 vf[2];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f16x4 lo = *(const f16x4*)(p_buf + ((rb * kWaves + 2 * ks) * 64 + lane) * 8);
-        const f16x4 hi = *(const f16x4*)(p_buf + ((rb * kWaves + 2 * ks + 1) * 64 + lane) * 8);
-        pa[rb] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      bool keep[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int page = pb + kPagesPerStep * t + 2 * ks + (e >> 2);
-        const int key = kPageSize * page + 4 * g + (e & 3);
-        keep[e] = !mask_v || (page < pe && key < L);
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 2; ++db) {
         const unsigned off = vrow + 2u * ks * kPageBytes + ((unsigned)(kDimsPerWave * w + 16 * db) ^ vsw);
         const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sp + off));
-        f16x8 vf = fp8x8_to_f16((unsigned)raw[0], (unsigned)raw[1]);
-        if (mask_v) {
+        vf[db] = fp8x8_to_f16((unsigned)raw[0], (unsigned)raw[1]);
+      }
+      if constexpr (kTail) {
+        // keys of pages past the segment (never loaded: stale or uninitialised
+        // LDS) and past the sequence end get V = 0, so P = 0 never meets a NaN
+        if (t == n_steps - 1) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = keep[e] ? vf[e] : (_Float16)0.f;
+          for (int e = 0; e < 8; ++e) {
+            const int page = pb + kPagesPerStep * t + 2 * ks + (e >> 2);
+            const int key = kPageSize * page + 4 * g + (e & 3);
+            const bool keep = page < pe && key < L;
+            vf[0][e] = keep ? vf[0][e] : (_Float16)0.f;
+            vf[1][e] = keep ? vf[1][e] : (_Float16)0.f;
+          }
         }
+      }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb], vf, acc[rb][db], 0, 0, 0);
+      for (int rb = 0; rb < NRB; ++rb) {
+        const f16x4 lo = *(const f16x4*)(p_buf + ((rb * kPagesPerStep + 2 * ks) * 64 + lane) * 8);
+        const f16x4 hi = *(const f16x4*)(p_buf + ((rb * kPagesPerStep + 2 * ks + 1) * 64 + lane) * 8);
+        const f16x8 pa = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[0], acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[1], acc[rb][1], 0, 0, 0);
       }
     }
-  }
+
+    // ---- scores of step t+1 (its pages landed before the barrier above)
+    if (kTail || t + 4 >= n_steps)
+      score_step(t + 1, sv, std::true_type{});
+    else
+      score_step(t + 1, sv, std::false_type{});
+  };
+
+  int t = 0;
+  for (; t + 3 < n_steps; ++t) step(t, std::false_type{});
+  for (; t < n_steps; ++t) step(t, std::true_type{});
 
   // ---- partials of this segment: m is identical in every wave; l sums the
-  // waves' key subsets in a fixed order; each wave writes its own dims of acc.
-  __syncthreads();   // all transfers have landed (last step waited vmcnt(0)); LDS is free
-  float* lsum = (float*)smem;                 // [wave][row]
-  float* mrow = lsum + kWaves * C::kRows;     // [row]
+  // page slots' key subsets in a fixed order; each wave writes its own dims.
+  __syncthreads();   // all transfers have landed (last wait was vmcnt(0)); LDS is free
+  float* lsum = (float*)smem;                     // [page slot][row]
+  float* mrow = lsum + kPagesPerStep * C::kRows;  // [row]
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float l = l_lane[rb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (g == 0) {
-      lsum[w * C::kRows + 16 * rb + n] = l;
-      if (w == 0) mrow[16 * rb + n] = m_ref[rb];
+  for (int j = 0; j < JMAX; ++j) {
+    if (scored(j)) {
+      float l = l_lane[j];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (g == 0) lsum[pw * C::kRows + 16 * (hf + 2 * j) + n] = l;
     }
+  }
+  if (w == 0 && g == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) mrow[16 * rb + n] = m_ref[rb];
   }
   __syncthreads();
 
@@ -417,24 +470,69 @@ splitkv_main_kernel(MainParams p) {
     const int row = tid;
     float l = lsum[row];
 #pragma unroll
-    for (int v = 1; v < kWaves; ++v) l += lsum[v * C::kRows + row];
+    for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
     const int i = row / G, gg = row - (row / G) * G;
-    float* dst = p.ws_ml + (((int64_t)seg * T + q0 + i) * Hq + h * G + gg) * 2;
+    float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
     dst[0] = mrow[row];
     dst[1] = l;
   }
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rb + 4 * g + r;
       if (row < rows) {
         const int i = row / G, gg = row - (row / G) * G;
-        float* dst = p.ws_acc + (((int64_t)seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + kDimsPerWave * w + n;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dst[16 * db] = acc[rb][db][r];
+        float* dst = p.ws_acc + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim +
+                     kDimsPerWave * w + n;
+        dst[0] = acc[rb][0][r];
+        dst[16] = acc[rb][1][r];
       }
     }
+}
+
+template <int G>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+splitkv_main_kernel(MainParams p) {
+  using C = Cfg<G>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
+
+  const const_i32* cu = (const const_i32*)p.cu_seqlens_q;
+  const const_i32* sl = (const const_i32*)p.seq_lens;
+  Geo geo;
+  geo.seg = blockIdx.x;
+  geo.b = blockIdx.y;
+  geo.h = blockIdx.z;
+  // out-of-contract values are clamped so that every access stays in its buffer
+  geo.q0 = cu[geo.b];
+  int q_len = cu[geo.b + 1] - geo.q0;
+  if (geo.q0 < 0 || geo.q0 >= p.total_q) q_len = 0;
+  q_len = min(max(q_len, 0), min(kMaxQLen, p.total_q - max(geo.q0, 0)));
+  if (q_len <= 0) return;
+  geo.q_len = q_len;
+  geo.L = min(max(sl[geo.b], 0), p.max_pages_per_seq * kPageSize);
+  const int pages = (geo.L + kPageSize - 1) / kPageSize;
+  const int chunk = (pages + p.num_segments - 1) / p.num_segments;
+  geo.pb = min(geo.seg * chunk, pages);
+  geo.pe = min(geo.pb + chunk, pages);
+  geo.rows = G * q_len;
+  geo.n_steps = (geo.pe - geo.pb + kPagesPerStep - 1) / kPagesPerStep;
+  geo.c2 = *(const const_f32*)p.k_descale * p.score_scale_log2;
+
+  const int nrb = (geo.rows + 15) >> 4;
+  if constexpr (G == 16) {
+    switch (nrb) {
+      case 1: verify_segment<16, 1>(p, geo, smem); break;
+      case 2: verify_segment<16, 2>(p, geo, smem); break;
+      case 3: verify_segment<16, 3>(p, geo, smem); break;
+      default: verify_segment<16, 4>(p, geo, smem); break;
+    }
+  } else {
+    if (nrb == 1)
+      verify_segment<8, 1>(p, geo, smem);
+    else
+      verify_segment<8, 2>(p, geo, smem);
+  }
 }
 
 }  // namespace
