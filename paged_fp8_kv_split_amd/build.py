@@ -66,9 +66,9 @@ def check_device_asm(asm: str, source: str) -> None:
             # and the restore right after the transfer
             nxt = lines[k + 1] if k + 1 < len(lines) else ""
             prev = lines[k - 1] if k > 0 else ""
-            if nxt.startswith("s_nop") and lines[k + 2].startswith("global_load_lds_dwordx4"):
+            if nxt.startswith("s_nop") and lines[k + 2].startswith("global_load_lds_dword"):
                 continue
-            if prev.startswith("global_load_lds_dwordx4"):
+            if prev.startswith("global_load_lds_dword"):
                 continue
             raise RuntimeError(f"{source}: unexpected M0 write: {line}")
 

@@ -81,6 +81,18 @@ def test_segment_count_independence(segments):
     assert diff <= 0.05 * sigma, diff
 
 
+@pytest.mark.parametrize("segments", [1, 2, 5])
+def test_long_segments_parity(segments):
+    # 20000 tokens in one to five segments: hundreds of steps per work-group,
+    # several 64-step windows of cached page ids per wave
+    w = Workload(name="longseg", ctx=(20000, 4100, 33), q_lens=(4, 1, 2), num_q_heads=16, num_kv_heads=1,
+                 num_segments=segments, seed=36)
+    case = make_case(w, "cpu").to(DEV)
+    out = run(case, num_segments=segments)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), f"long segments S={segments}")
+
+
 # ------------------------------------------------------------------ full-size shapes, sampled rows
 @pytest.mark.parametrize("name", ["prod", "gqa8", "long", "occupancy"])
 def test_full_size_sampled(name):
