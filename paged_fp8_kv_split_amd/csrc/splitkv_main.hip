@@ -364,13 +364,41 @@ __device__ __forceinline__ void wave_main(const MainParams& p, const Geo& geo, u
   int* const flag = (int*)(smem + C::kOffFlag);   // one word per step, 4 in rotation
   if (tid < 4) flag[tid] = 0;
 
-  // step 0 has landed in every wave (later steps may still fly): score it
-  lds_barrier();
+  // softmax of a step whose raw scores are in sv (stage st): slow-path flag (a
+  // raw score above its row's threshold) and P = 2^(s c2 - m) against the
+  // current reference max, published to LDS and kept in pv for the row sums.
   f32x4 sv[NJA];
+  f16x4 pv[NJA];
+  auto softmax = [&](int st) {
+    if constexpr (NJ > 0) {
+      bool over = false;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) over |= sv[j][r] > thr[j];
+      if (__any(over) && lane == 0) flag[st] = 1;
+      uint8_t* const pb_ = smem + C::kOffP + (st & 1) * C::kPBytes + 8 * lane;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float mref = m_ref[HF + 2 * j] == -__builtin_inff() ? 0.f : m_ref[HF + 2 * j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[j][r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[j][r], c2, -mref));
+        *(f16x4*)(pb_ + ((HF + 2 * j) * 4 + pw) * 512) = pv[j];
+      }
+    }
+  };
+
+  // step 0 has landed in every wave (later steps may still fly): score it.
+  // The two halves of the work-group order their work differently so that a
+  // SIMD's two waves overlap VALU with MFMA work: half 0 does softmax(t),
+  // barrier, P V(t), scores(t+1); half 1 does barrier, scores(t+1),
+  // softmax(t+1), P V(t) -- so half 1 computes softmax(0) here.
+  lds_barrier();
   if (n_steps > 4)
     score_step(0, 0, sv, std::false_type{});
   else
     score_step(0, 0, sv, std::true_type{});
+  if (HF == 1) softmax(0);
 
   // One step: softmax of step t, barrier, P V of step t and the scores of step
   // t+1. Steady-state steps (t + 4 < n_steps) have every page of steps t to
@@ -383,24 +411,7 @@ __device__ __forceinline__ void wave_main(const MainParams& p, const Geo& geo, u
     const int buf = st & 1;
     const unsigned p_buf = p_lane + buf * C::kPBytes;
 
-    // ---- softmax of step t: slow-path flag (a raw score above its row's
-    // threshold), P = 2^(s c2 - m) against the current reference max
-    f16x4 pv[NJA];
-    if constexpr (NJ > 0) {
-      bool over = false;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) over |= sv[j][r] > thr[j];
-      if (__any(over) && lane == 0) flag[st] = 1;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const float mref = m_ref[HF + 2 * j] == -__builtin_inff() ? 0.f : m_ref[HF + 2 * j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[j][r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[j][r], c2, -mref));
-        *(f16x4*)(smem + (p_buf - lds_addr(smem)) + ((HF + 2 * j) * 4 + pw) * 512) = pv[j];
-      }
-    }
+    if (HF == 0) softmax(st);
     if (w == 0 && lane == 0) flag[(st + 2) & 3] = 0;   // last read two steps ago
 
     // K of step t+1 and V of step t must have landed (two later steps may fly)
@@ -497,25 +508,36 @@ __device__ __forceinline__ void wave_main(const MainParams& p, const Geo& geo, u
       l_lane[j] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[j], false), false);
     }
 
+    auto pv_mfma = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const uint8_t* pr = smem + (p_buf - lds_addr(smem)) + (rb * 4 + 2 * ks) * 512;
-        const f16x4 lo = *(const f16x4*)pr;
-        const f16x4 hi = *(const f16x4*)(pr + 512);
-        const f16x8 pa = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[ks][0], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[ks][1], acc[rb][1], 0, 0, 0);
+        for (int rb = 0; rb < NRB; ++rb) {
+          const uint8_t* pr = smem + (p_buf - lds_addr(smem)) + (rb * 4 + 2 * ks) * 512;
+          const f16x4 lo = *(const f16x4*)pr;
+          const f16x4 hi = *(const f16x4*)(pr + 512);
+          const f16x8 pa = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[ks][0], acc[rb][0], 0, 0, 0);
+          acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[ks][1], acc[rb][1], 0, 0, 0);
+        }
       }
-    }
-
+    };
     // ---- scores of step t+1 (its K landed before the barrier above)
-    const int kst = (st + 1) & 3;
-    if (kTail || t + 5 >= n_steps)
-      score_step(t + 1, kst, sv, std::true_type{});
-    else
-      score_step(t + 1, kst, sv, std::false_type{});
+    auto scores_next = [&]() {
+      const int kst = (st + 1) & 3;
+      if (kTail || t + 5 >= n_steps)
+        score_step(t + 1, kst, sv, std::true_type{});
+      else
+        score_step(t + 1, kst, sv, std::false_type{});
+    };
+    if constexpr (HF == 0) {
+      pv_mfma();
+      scores_next();
+    } else {
+      scores_next();
+      if (!kTail || t + 1 < n_steps) softmax((st + 1) & 3);
+      pv_mfma();
+    }
   };
 
   int t = 0;
