@@ -130,6 +130,13 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
     return fail(PFKV_INVALID, "q / out strides must be positive");
   if (a->q_stride_token % 8 || a->q_stride_head % 8 || !aligned(a->q, 16))
     return fail(PFKV_INVALID, "q rows must be 16-byte aligned (strides multiple of 8 elements)");
+  {
+    // the main kernel addresses a (sequence, KV head)'s Q rows with 32-bit byte offsets
+    const int64_t group = a->num_q_heads / a->num_kv_heads;
+    const int64_t span = ((int64_t)(pfkv::kMaxQLen - 1) * a->q_stride_token + (group - 1) * a->q_stride_head +
+                          pfkv::kHeadDim) * 2;
+    if (span >= ((int64_t)1 << 32)) return fail(PFKV_INVALID, "q strides too large (a KV head's rows span >= 4 GiB)");
+  }
   if (a->out_stride_token % 4 || a->out_stride_head % 4 || !aligned(a->out, 8))
     return fail(PFKV_INVALID, "out rows must be 8-byte aligned (strides multiple of 4 elements)");
   if (!aligned(a->workspace, 16)) return fail(PFKV_INVALID, "workspace must be 16-byte aligned");

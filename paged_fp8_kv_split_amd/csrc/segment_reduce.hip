@@ -6,14 +6,17 @@
 // For output row (t, hq) with segments s = 0 .. S-1 holding (m_s, l_s, acc_s):
 //   M = max_s m_s,  w_s = 2^(m_s - M) (0 for an empty segment, m_s = -inf),
 //   out = v_descale * sum_s w_s acc_s / sum_s w_s l_s   (0 when the sum is 0),
-// summed in the fixed order s = 0, 1, ..., then rounded to bf16 to nearest even.
-// One wave per output row, four dims per lane (coalesced 1 KiB reads per segment).
+// then rounded to bf16 to nearest even. The numerator is summed in the order
+// s = 0, 1, ...; the denominator by a fixed butterfly over the wave's lanes.
+// One wave per output row: lane s holds (m_s, l_s), every lane four dims of
+// the accumulators, whose loads for up to 16 segments are in flight together.
 #include "pfkv_internal.h"
 
 namespace pfkv {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(4))) const float const_f32;
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -22,6 +25,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+constexpr int kBatch = 16;   // segments whose accumulator loads fly together
+
 __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -29,20 +38,32 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= rows_total) return;
   const int S = p.num_segments;
-  const const_f32* ml = (const const_f32*)p.ws_ml;
 
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(s * rows_total + row) * 2]);
+  float m = -__builtin_inff(), l = 0.f;
+  if (lane < S) {
+    const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
+    m = v[0];
+    l = v[1];
+  }
+  float M = m;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+  const float wgt = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  float den = wgt * l;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) den += __shfl_xor(den, k, 64);
 
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float m = ml[(s * rows_total + row) * 2];
-    const float l = ml[(s * rows_total + row) * 2 + 1];
-    const float wgt = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    den += wgt * l;
-    const f32x4 a = *(const f32x4*)(p.ws_acc + (s * rows_total + row) * kHeadDim + 4 * lane);
-    num += wgt * a;
+  const float* acc = p.ws_acc + row * kHeadDim + 4 * lane;
+  const int64_t seg_stride = rows_total * kHeadDim;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    f32x4 a[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f32x4*)(acc + (s0 + k) * seg_stride));
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (s0 + k < S) num += lane_value(wgt, s0 + k) * a[k];
   }
   const float vd = *(const const_f32*)p.v_descale;
   const float inv = den > 0.f ? vd / den : 0.f;

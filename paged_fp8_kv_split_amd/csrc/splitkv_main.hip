@@ -122,11 +122,15 @@ __device__ __forceinline__ void dma_4b(const void* sbase, unsigned voff, unsigne
 }
 
 // Wait until at most `pending` of this wave's vector-memory operations are in
-// flight (0, 4 or 8). Inside the main loop the only such operations are the
-// page transfers (four 1 KiB transfers per wave and step) and the page-id
-// window refills, which are older than the transfers they precede.
+// flight (0, 4, 8, 12 or 16). Inside the main loop the only such operations
+// are the page transfers (four 1 KiB transfers per wave and step) and the
+// page-id window refills, which are older than the transfers they precede.
 __device__ __forceinline__ void wait_vm(int pending) {
-  if (pending >= 8)
+  if (pending >= 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (pending >= 12)
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (pending >= 8)
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else if (pending >= 4)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -231,11 +235,6 @@ struct PageStream {
   }
 };
 
-__device__ __forceinline__ bool flag_up(const uint8_t* smem, int off_flag, int t) {
-  const unsigned word = *(const unsigned*)(smem + off_flag + 4 * (t & 1));
-  return __builtin_amdgcn_readfirstlane(word) != 0;
-}
-
 // Score wave w (page slot w): K stream, S^T = K Q^T for all NRB row blocks,
 // lazy softmax, P to LDS, row sums; writes m and l of the segment.
 template <int G, int NRB>
@@ -252,47 +251,50 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   PageStream ks;
   ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
 
-  // ---- prologue: K of steps 0-2 (ids by scalar loads), the first page-id
-  // window and Q fly together.
+  // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
+  // phase 1) by page-style transfers, 16-byte chunk c of row r at position
+  // c ^ (r & 15), score wave w moving rows 16w..16w+15; K of steps 0-2 (block-
+  // table entries by scalar loads) and the first page-id window follow. Only
+  // Q and step 0 are waited for; Q moves to registers after the first barrier.
+  uint8_t* const q_stage = smem + C::kOffStage + (kStages + 2) * kStageBytes;
   if (n_steps > 0) {
+    if (w < NRB) {
+      const uint8_t* q_base = (const uint8_t*)(p.q + (int64_t)q0 * p.q_stride_token + (int64_t)h * G * p.q_stride_head);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 16 * w + 2 * k + (lane >> 5);
+        const int rr = r < rows ? r : 0;            // padding rows read row 0, zeroed in registers
+        const int i = rr / G, gg = rr - (rr / G) * G;
+        const unsigned voff = (unsigned)((i * p.q_stride_token + gg * p.q_stride_head) * 2) + 16u * ((lane & 31) ^ (r & 15));
+        dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + 2 * k) * 512);
+      }
+    }
     ks.fetch_window(0, lane);
     const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
     if (ks.has(0)) ks.put(0, id0);
     if (ks.has(1)) ks.put(1, id1);
     if (ks.has(2)) ks.put(2, id2);
+    wait_vm(ks.count(1) + ks.count(2));
+    ks.next_id = ks.read_id(3);
   }
   // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
-  // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8.
+  // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
   bf16x8 qop[NRB][4][2];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int r = 16 * rb + n;
-    const int rr = r < rows ? r : 0;                 // padding rows read row 0, zeroed below
-    const int i = rr / G, gg = rr - (rr / G) * G;
-    const uint16_t* src = p.q + (int64_t)(q0 + i) * p.q_stride_token + (int64_t)(h * G + gg) * p.q_stride_head;
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = 16 * rb + n;
+      const bool pad = r >= rows;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) qop[rb][u][hh] = *(const bf16x8*)(src + 16 * (4 * u + g) + 8 * hh);
-  }
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const bool pad = 16 * rb + n >= rows;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) qop[rb][u][hh] = pad ? bf16x8{} : qop[rb][u][hh];
-  }
-  // Keep the Q loads before the waits below (the compiler waits for them
-  // where it first reads qop).
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) asm volatile("" : "+v"(qop[rb][u][hh]) :: "memory");
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  ks.next_id = ks.read_id(3);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int pos = (8 * u + 2 * g + hh) ^ n;
+          const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
+          qop[rb][u][hh] = pad ? bf16x8{} : v;
+        }
+    }
+  };
 
   // ---- per-lane LDS addresses
   const unsigned kcol = 16u * ((g ^ n ^ (12 * (w & 1))) & 15);
@@ -317,10 +319,11 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     l_lane[rb] = 0.f;
   }
 
-  // raw scores of this wave's page of step t (K stage kst). In tail steps the
-  // page may be missing and keys past a row's causal limit (or the sequence
-  // end) are masked to -inf; steady-state steps need neither.
-  auto score_step = [&](int t, int kst, auto tail) {
+  // raw scores of this wave's page of step t from its K block (kraw, read
+  // from LDS by the caller). In tail steps the page may be missing and keys
+  // past a row's causal limit (or the sequence end) are masked to -inf;
+  // steady-state steps need neither.
+  auto score_step = [&](int t, const u32x4 (&kraw)[4], auto tail) {
     constexpr bool kTail = decltype(tail)::value;
     const int pidx = pb + kPagesPerStep * t + w;
     if (!kTail || ks.has(t)) {
@@ -328,9 +331,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       for (int rb = 0; rb < NRB; ++rb) sv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 raw = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
-        const bf16x8 k0 = fp8x8_to_bf16(raw[0], raw[1]);
-        const bf16x8 k1 = fp8x8_to_bf16(raw[2], raw[3]);
+        const bf16x8 k0 = fp8x8_to_bf16(kraw[u][0], kraw[u][1]);
+        const bf16x8 k1 = fp8x8_to_bf16(kraw[u][2], kraw[u][3]);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rb][u][0], sv[rb], 0, 0, 0);
@@ -355,10 +357,21 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
   };
 
-  // P of step u (scores in sv), after the slow path if any score wave raised
-  // its flag for step u.
-  auto form_p = [&](int u, int pbuf, bool slow) {
-    if (slow) {
+  // P of step u (scores in sv). P is first formed against the current m,
+  // while the flag word (any score wave saw a row pass its threshold in step
+  // u) is still in flight; in the rare slow path it is formed again.
+  auto form_p = [&](int u, int pbuf, unsigned flag_word) {
+    f16x4 pv[NRB];
+    auto exps = [&]() {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[rb][r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2, -mref));
+      }
+    };
+    exps();
+    if (__builtin_amdgcn_readfirstlane(flag_word) != 0) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         float v = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
@@ -381,35 +394,42 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         l_lane[rb] *= alpha;
         if (w == 0 && g == 0) alpha_buf[(u & 1) * C::kRows + 16 * rb + n] = alpha;
       }
+      exps();
     }
     const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
-      f16x4 pv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2, -mref));
-      *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = pv;
-      const f16x2 lo = {pv[0], pv[1]}, hi = {pv[2], pv[3]};
+      *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = pv[rb];
+      const f16x2 lo = {pv[rb][0], pv[rb][1]}, hi = {pv[rb][2], pv[rb][3]};
       l_lane[rb] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[rb], false), false);
     }
   };
 
   // Phase t: P of step t-1, K transfer of step t+3, scores and flag of step
-  // t, wait for K of step t+1, barrier. Steady-state phases (4 <= t,
-  // t + 4 < n_steps) have full steps t..t+3, no masking, and the ring stage
-  // ST = t % 4 as a compile-time constant.
+  // t, wait for K of step t+1, barrier. The LDS reads of the phase (flag word,
+  // K block) are issued first. Steady-state phases (4 <= t, t + 4 < n_steps)
+  // have full steps t..t+3, no masking, and the ring stage ST = t % 4 as a
+  // compile-time constant.
   auto phase = [&](int t, auto tail, auto stage) {
     constexpr bool kTail = decltype(tail)::value;
     constexpr int kSt = decltype(stage)::value;
     const int kst = kSt >= 0 ? kSt : (t & 3);
-    if (!kTail || (t >= 1 && t <= n_steps)) form_p(t - 1, (kst + 3) & 1, flag_up(smem, C::kOffFlag, t - 1));
+    const bool have_p = !kTail || (t >= 1 && t <= n_steps);
+    const bool have_s = !kTail || t < n_steps;
     ks.issue(t + 3, lane);
-    if (!kTail || t < n_steps) {
+    unsigned flag_word = 0;
+    if (have_p) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((kst + 3) & 1));
+    u32x4 kraw[4];
+    if (!kTail || ks.has(t)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kraw[u] = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
+    }
+    if (have_p) form_p(t - 1, (kst + 3) & 1, flag_word);
+    if (have_s) {
       if (kTail && t + 2 >= n_steps)
-        score_step(t, kst, std::true_type{});
+        score_step(t, kraw, std::true_type{});
       else
-        score_step(t, kst, std::false_type{});
+        score_step(t, kraw, std::false_type{});
       bool over = false;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
@@ -426,7 +446,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   };
 
   if (n_steps > 0) {
-    lds_barrier();   // step 0's K is in LDS in every score wave
+    lds_barrier();   // Q and step 0's K are in LDS
+    load_q();
     int t = 0;
     for (; t < 4 && t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
     for (; t + 7 < n_steps; t += 4) {
@@ -460,8 +481,9 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
     const int i = row / G, gg = row - (row / G) * G;
     float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
-    dst[0] = mrow[row];
-    dst[1] = l;
+    // streaming stores: the partials are read once, by the reduce
+    __builtin_nontemporal_store(mrow[row], dst);
+    __builtin_nontemporal_store(l, dst + 1);
   }
 }
 
@@ -484,7 +506,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     vs.fetch_window(0, lane);
     const int id0 = vs.first_id(0);
     if (vs.has(0)) vs.put(0, id0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm(vs.count(0));   // the window
     vs.next_id = vs.read_id(1);
   }
 
@@ -511,29 +533,46 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   bool slow1 = false;   // flag of step t-1 in phase t
   bool slow2 = false;   // flag of step t-2 in phase t
 
-  // Phase t: extra barrier if step t-1 takes the slow path, V transfer of
-  // step t+1, O += P V of step t-2 (rescaled first if step t-2 moved m), wait
-  // for V of step t-1, barrier.
+  // Phase t: the LDS reads of step t-2 (V block, P) and of the flag word of
+  // step t-1 first; an extra barrier if step t-1 takes the slow path; the V
+  // transfer of step t+1; O += P V of step t-2 (rescaled first if step t-2
+  // moved m); wait for V of step t-1; barrier.
   auto phase = [&](int t, auto tail, auto stage) {
     constexpr bool kTail = decltype(tail)::value;
     constexpr int kSt = decltype(stage)::value;
-    slow2 = slow1;
-    slow1 = (!kTail || (t >= 1 && t <= n_steps)) ? flag_up(smem, C::kOffFlag, t - 1) : false;
-    if (slow1) lds_barrier();   // matches the score waves' maxima exchange
+    const bool have_f = !kTail || (t >= 1 && t <= n_steps);
+    const bool have_pv = !kTail || (t >= 2 && t - 2 < n_steps);
+    const int u = t - 2;
+    const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
+    const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
     vs.issue(t + 1, lane);
-    if (!kTail || (t >= 2 && t - 2 < n_steps)) {
-      const int u = t - 2;
-      const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
-      // k-slot 8g + e of k-step ks is key 4g + (e & 3) of page slot 2 ks + (e >> 2)
+    unsigned flag_word = 0;
+    if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
+    // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
+    i32x2 vraw[2][4];
+    f16x8 pa[NRB][2];
+    if (have_pv) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          vraw[kk][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(smem + v_off[db] + vst * kStageBytes + kk * 2 * kPageBytes));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          pa[rb][kk] = *(const f16x8*)(smem + p_off + pbuf * C::kPBytes + (rb * 2 + kk) * (64 * 16));
+    }
+    slow2 = slow1;
+    slow1 = have_f && __builtin_amdgcn_readfirstlane(flag_word) != 0;
+    if (slow1) lds_barrier();   // matches the score waves' maxima exchange
+    if (have_pv) {
       f16x8 vf[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)(smem + v_off[db] + vst * kStageBytes + kk * 2 * kPageBytes));
-          vf[kk][db] = fp8x8_to_f16((unsigned)raw[0], (unsigned)raw[1]);
-        }
+        for (int db = 0; db < 4; ++db) vf[kk][db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
       if constexpr (kTail) {
         // keys of pages past the segment (never loaded: stale or uninitialised
         // LDS) and past the sequence end get V = 0, so P = 0 never meets a NaN
@@ -560,16 +599,13 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
             for (int r = 0; r < 4; ++r) acc[rb][db][r] *= a[r];
         }
       }
-      const int pbuf = u & 1;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const f16x8 pa = *(const f16x8*)(smem + p_off + pbuf * C::kPBytes + (rb * 2 + kk) * (64 * 16));
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int db = 0; db < 4; ++db)
-            acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[kk][db], acc[rb][db], 0, 0, 0);
-        }
+            acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
     }
     if constexpr (kTail)
       wait_vm(vs.count(t) + vs.count(t + 1));
@@ -603,7 +639,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         const int i = row / G, gg = row - (row / G) * G;
         float* dst = p.ws_acc + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + kVDims * v + n;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dst[16 * db] = acc[rb][db][r];
+        for (int db = 0; db < 4; ++db) __builtin_nontemporal_store(acc[rb][db][r], dst + 16 * db);
       }
     }
 }

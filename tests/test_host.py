@@ -82,6 +82,8 @@ CASES = [
     ("table stride", dict(block_table_stride=100), "gfx950", INVALID),
     ("q stride odd", dict(q_stride_head=255), "gfx950", INVALID),
     ("q misaligned", dict(q=0x100008), "gfx950", INVALID),
+    ("q rows span 4 GiB", dict(q_stride_token=1 << 30), "gfx950", INVALID),
+    ("q rows just under 4 GiB", dict(q_stride_token=((1 << 31) // 3 - 4096) // 8 * 8), "gfx950", 0),
     ("out stride", dict(out_stride_head=2), "gfx950", INVALID),
     ("workspace misaligned", dict(workspace=0x180004), "gfx950", INVALID),
     ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
