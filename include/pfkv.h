@@ -112,7 +112,14 @@ int pfkv_segment_reduce(const pfkv_args* args, void* stream);
  */
 int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
 
-/* Workspace bytes for S segments: S * total_q * num_q_heads * (head_dim 256 + 2) * 4. 0 for bad sizes. */
+/*
+ * Workspace bytes for S segments: S * total_q * num_q_heads * 520. 0 for bad
+ * sizes. Layout (after the main kernel): fp16 o[S][total_q][num_q_heads][256],
+ * the segment's softmax-weighted mean of V (without v_descale, 0 for a segment
+ * with no visible key), then fp32 (m, l)[S][total_q][num_q_heads], m the
+ * segment's reference max of the scores in log2 units (-inf when empty) and
+ * l the sum of 2^(score - m) over its keys.
+ */
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads);
 
 /* Text of the most recent failure on this host thread ("" if none). Valid until the next call. */

@@ -94,7 +94,7 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads) {
 
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads) {
   if (num_segments <= 0 || total_q <= 0 || num_q_heads <= 0) return 0;
-  return (uint64_t)num_segments * (uint64_t)total_q * (uint64_t)num_q_heads * (pfkv::kHeadDim + 2) * 4u;
+  return (uint64_t)num_segments * (uint64_t)total_q * (uint64_t)num_q_heads * pfkv::kPartialBytes;
 }
 
 int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
@@ -201,8 +201,9 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   }
 
   const int group = a->num_q_heads / a->num_kv_heads;
-  float* ws = (float*)a->workspace;
-  const uint64_t acc_floats = (uint64_t)a->num_segments * a->total_q * a->num_q_heads * pfkv::kHeadDim;
+  const uint64_t part_rows = (uint64_t)a->num_segments * a->total_q * a->num_q_heads;
+  uint16_t* ws_o = (uint16_t*)a->workspace;
+  float* ws_ml = (float*)(ws_o + part_rows * pfkv::kHeadDim);
 
   *mp = pfkv::MainParams();
   *rp = pfkv::ReduceParams();
@@ -217,8 +218,8 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.seq_lens = a->seq_lens;
   m.cu_seqlens_q = a->cu_seqlens_q;
   m.k_descale = a->k_descale;
-  m.ws_acc = ws;
-  m.ws_ml = ws + acc_floats;
+  m.ws_o = ws_o;
+  m.ws_ml = ws_ml;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;
   m.num_q_heads = a->num_q_heads;
@@ -228,8 +229,8 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.num_segments = a->num_segments;
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
 
-  rp->ws_acc = ws;
-  rp->ws_ml = ws + acc_floats;
+  rp->ws_o = ws_o;
+  rp->ws_ml = ws_ml;
   rp->v_descale = a->v_descale;
   rp->out = (uint16_t*)a->out;
   rp->out_stride_token = a->out_stride_token;

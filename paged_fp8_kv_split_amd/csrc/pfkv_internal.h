@@ -11,10 +11,13 @@ constexpr int kPageSize = 16;   // tokens per KV page
 constexpr int kMaxQLen = 4;     // query tokens per sequence
 constexpr int kMaxSegments = 64;
 
-// Workspace layout (fp32), written by the main kernel and read by the reduce:
-//   acc [S][T][Hq][256]  un-normalized sum of p * V (V without its descale)
-//   ml  [S][T][Hq][2]    (m, l): reference max in log2 units and sum of p
-// so that segment s contributes  2^(m_s - M) * acc_s / sum_s 2^(m_s - M) * l_s.
+// Workspace layout, written by the main kernel and read by the reduce:
+//   o  [S][T][Hq][256] fp16  the segment's softmax-weighted mean of V (V without
+//                            its descale): sum p V / sum p, 0 when sum p = 0
+//   ml [S][T][Hq][2]   fp32  (m, l): reference max in log2 units and l = sum p
+// so that segment s contributes  2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
+constexpr int kPartialBytes = kHeadDim * 2 + 2 * 4;   // workspace bytes per (segment, token, head)
+
 struct MainParams {
   const uint16_t* q;           // bf16 bits
   int64_t q_stride_token, q_stride_head;
@@ -25,14 +28,14 @@ struct MainParams {
   const int32_t* seq_lens;
   const int32_t* cu_seqlens_q;
   const float* k_descale;
-  float* ws_acc;
+  uint16_t* ws_o;              // fp16 bits
   float* ws_ml;
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
 };
 
 struct ReduceParams {
-  const float* ws_acc;
+  const uint16_t* ws_o;        // fp16 bits
   const float* ws_ml;
   const float* v_descale;
   uint16_t* out;               // bf16 bits

@@ -3,13 +3,13 @@
 // head_dim 256 fp8 paged KV", section Modifications: a split-KV segment reduce
 // after the main kernel).
 //
-// For output row (t, hq) with segments s = 0 .. S-1 holding (m_s, l_s, acc_s):
-//   M = max_s m_s,  w_s = 2^(m_s - M) (0 for an empty segment, m_s = -inf),
-//   out = v_descale * sum_s w_s acc_s / sum_s w_s l_s   (0 when the sum is 0),
+// For output row (t, hq) with segments s = 0 .. S-1 holding (m_s, l_s, o_s):
+//   M = max_s m_s,  c_s = 2^(m_s - M) l_s (0 for an empty segment, m_s = -inf),
+//   out = v_descale * sum_s c_s o_s / sum_s c_s   (0 when the sum is 0),
 // then rounded to bf16 to nearest even. The numerator is summed in the order
 // s = 0, 1, ...; the denominator by a fixed butterfly over the wave's lanes.
 // One wave per output row: lane s holds (m_s, l_s), every lane four dims of
-// the accumulators, whose loads for up to 16 segments are in flight together.
+// the fp16 o rows, whose loads for up to 16 segments are in flight together.
 #include "pfkv_internal.h"
 
 namespace pfkv {
@@ -17,6 +17,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const float const_f32;
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -29,7 +30,7 @@ __device__ __forceinline__ float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
-constexpr int kBatch = 16;   // segments whose accumulator loads fly together
+constexpr int kBatch = 16;   // segments whose o loads fly together
 
 __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -48,22 +49,22 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   float M = m;
 #pragma unroll
   for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
-  const float wgt = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M);
-  float den = wgt * l;
+  const float coef = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * l;
+  float den = coef;
 #pragma unroll
   for (int k = 1; k < 64; k <<= 1) den += __shfl_xor(den, k, 64);
 
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  const float* acc = p.ws_acc + row * kHeadDim + 4 * lane;
+  const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
   const int64_t seg_stride = rows_total * kHeadDim;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
-    f32x4 a[kBatch];
+    f16x4 a[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f32x4*)(acc + (s0 + k) * seg_stride));
+      if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (s0 + k < S) num += lane_value(wgt, s0 + k) * a[k];
+      if (s0 + k < S) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
   }
   const float vd = *(const const_f32*)p.v_descale;
   const float inv = den > 0.f ? vd / den : 0.f;

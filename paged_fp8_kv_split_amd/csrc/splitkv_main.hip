@@ -85,7 +85,9 @@ struct Cfg {
   static constexpr int kOffStage = (kOffIds + kWaves * 2 * 64 * 4 + 1023) & ~1023;   // K ring, then V ring
   static constexpr int kLdsBytes = kOffStage + 2 * kStages * kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert((kPagesPerStep + 1) * kRows * 4 <= kLdsBytes, "epilogue scratch");
+  static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][256]
+  static_assert((kPagesPerStep + 2) * kRows * 4 <= kOffObuf, "epilogue row sums");
+  static_assert(kOffObuf + kRows * kHeadDim * 2 <= kLdsBytes, "epilogue o staging");
 };
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -234,6 +236,19 @@ struct PageStream {
     }
   }
 };
+
+// Stores the staged fp16 o rows ([row][256] in LDS) of the work-group's
+// segment with 16-byte streaming stores, all 512 threads.
+template <int G>
+__device__ __forceinline__ void store_o(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
+  const int T = p.total_q, Hq = p.num_q_heads;
+  for (int idx = threadIdx.x; idx < geo.rows * 32; idx += kThreads) {
+    const int row = idx >> 5, c = idx & 31;
+    const int i = row / G, gg = row - (row / G) * G;
+    uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + geo.q0 + i) * Hq + geo.h * G + gg) * kHeadDim + 8 * c;
+    __builtin_nontemporal_store(*(const u32x4*)(obuf + row * 512 + 16 * c), (u32x4*)dst);
+  }
+}
 
 // Score wave w (page slot w): K stream, S^T = K Q^T for all NRB row blocks,
 // lazy softmax, P to LDS, row sums; writes m and l of the segment.
@@ -459,11 +474,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
   }
 
-  // ---- m and l of the segment: m is identical in every score wave; l sums
-  // the page slots' key subsets in a fixed order.
+  // ---- segment partials: m is identical in every score wave; l sums the
+  // page slots' key subsets in a fixed order; the P.V waves then divide their
+  // accumulators by l and stage fp16 o in LDS for full-row stores.
   __syncthreads();   // all transfers have landed; LDS is free
-  float* lsum = (float*)smem;                     // [slot][row]
-  float* mrow = lsum + kPagesPerStep * C::kRows;  // [row]
+  float* const lsum = (float*)smem;                     // [slot][row]
+  float* const mrow = lsum + kPagesPerStep * C::kRows;  // [row]
+  float* const ltot = mrow + C::kRows;                  // [row]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float l = l_lane[rb];
@@ -479,16 +496,20 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     float l = lsum[row];
 #pragma unroll
     for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
+    ltot[row] = l;
     const int i = row / G, gg = row - (row / G) * G;
     float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
     // streaming stores: the partials are read once, by the reduce
     __builtin_nontemporal_store(mrow[row], dst);
     __builtin_nontemporal_store(l, dst + 1);
   }
+  __syncthreads();   // l of every row visible to the P.V waves
+  __syncthreads();   // o staged
+  store_o<G>(p, geo, smem + C::kOffObuf);
 }
 
 // P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
-// NRB row blocks; writes its slice of the segment's accumulator.
+// NRB row blocks; stages its slice of the segment's normalised output o.
 template <int G, int NRB>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G>;
@@ -627,21 +648,25 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
   }
 
-  __syncthreads();   // matches the score waves' epilogue
+  __syncthreads();   // the score waves' epilogue: row sums, then l of every row
   __syncthreads();
-  const int T = p.total_q, Hq = p.num_q_heads;
+  __syncthreads();
+  const float* const ltot = (const float*)smem + (kPagesPerStep + 1) * C::kRows;
+  _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rb + 4 * g + r;
       if (row < rows) {
-        const int i = row / G, gg = row - (row / G) * G;
-        float* dst = p.ws_acc + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + kVDims * v + n;
+        const float l = ltot[row];
+        const float inv = l > 0.f ? 1.0f / l : 0.f;   // no visible key: o = 0
 #pragma unroll
-        for (int db = 0; db < 4; ++db) __builtin_nontemporal_store(acc[rb][db][r], dst + 16 * db);
+        for (int db = 0; db < 4; ++db) obuf[row * kHeadDim + kVDims * v + 16 * db + n] = (_Float16)(acc[rb][db][r] * inv);
       }
     }
+  __syncthreads();
+  store_o<G>(p, geo, smem + C::kOffObuf);
 }
 
 template <int G, int NRB>

@@ -120,9 +120,10 @@ def test_num_segments_heuristic(lib, cus, n, hkv, expect):
 
 
 def test_workspace_bytes(lib):
-    assert pfkv.workspace_bytes(16, 64, 16) == 16 * 64 * 16 * 258 * 4
+    # fp16 o[256] + fp32 (m, l) per (segment, token, head)
+    assert pfkv.workspace_bytes(16, 64, 16) == 16 * 64 * 16 * (256 * 2 + 8)
     assert pfkv.workspace_bytes(0, 64, 16) == 0
-    assert pfkv.workspace_bytes(64, 8, 32) == 64 * 8 * 32 * 258 * 4
+    assert pfkv.workspace_bytes(64, 8, 32) == 64 * 8 * 32 * (256 * 2 + 8)
 
 
 def test_stream_read_validation(lib):
