@@ -86,7 +86,7 @@ struct Cfg {
   static constexpr int kLdsBytes = kOffStage + 2 * kStages * kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][256]
-  static_assert((kPagesPerStep + 2) * kRows * 4 <= kOffObuf, "epilogue row sums");
+  static_assert(kPagesPerStep * kRows * 4 <= kOffObuf, "epilogue row sums");
   static_assert(kOffObuf + kRows * kHeadDim * 2 <= kLdsBytes, "epilogue o staging");
 };
 
@@ -263,14 +263,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   const float c2 = geo.c2;
   uint8_t* const k_ring = smem + C::kOffStage;
 
-  PageStream ks;
+  PageStream ks;   // K of page slot w: streamed by P.V wave w + 4, read here
   ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
 
   // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
   // phase 1) by page-style transfers, 16-byte chunk c of row r at position
-  // c ^ (r & 15), score wave w moving rows 16w..16w+15; K of steps 0-2 (block-
-  // table entries by scalar loads) and the first page-id window follow. Only
-  // Q and step 0 are waited for; Q moves to registers after the first barrier.
+  // c ^ (r & 15), score wave w moving rows 16w..16w+15, while the P.V waves
+  // start the K and V streams. Q moves to registers after the first barrier.
   uint8_t* const q_stage = smem + C::kOffStage + (kStages + 2) * kStageBytes;
   if (n_steps > 0) {
     if (w < NRB) {
@@ -284,13 +283,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + 2 * k) * 512);
       }
     }
-    ks.fetch_window(0, lane);
-    const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
-    if (ks.has(0)) ks.put(0, id0);
-    if (ks.has(1)) ks.put(1, id1);
-    if (ks.has(2)) ks.put(2, id2);
-    wait_vm(ks.count(1) + ks.count(2));
-    ks.next_id = ks.read_id(3);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
   // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
@@ -420,8 +413,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
   };
 
-  // Phase t: P of step t-1, K transfer of step t+3, scores and flag of step
-  // t, wait for K of step t+1, barrier. The LDS reads of the phase (flag word,
+  // Phase t: P of step t-1, scores and flag of step t, barrier. The LDS reads of the phase (flag word,
   // K block) are issued first. Steady-state phases (4 <= t, t + 4 < n_steps)
   // have full steps t..t+3, no masking, and the ring stage ST = t % 4 as a
   // compile-time constant.
@@ -431,7 +423,6 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     const int kst = kSt >= 0 ? kSt : (t & 3);
     const bool have_p = !kTail || (t >= 1 && t <= n_steps);
     const bool have_s = !kTail || t < n_steps;
-    ks.issue(t + 3, lane);
     unsigned flag_word = 0;
     if (have_p) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((kst + 3) & 1));
     u32x4 kraw[4];
@@ -453,11 +444,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       const bool any = __any(over);
       if (lane == 0) smem[C::kOffFlag + 4 * (kst & 1) + w] = any ? 1 : 0;
     }
-    if constexpr (kTail)
-      wait_vm(ks.count(t + 2) + ks.count(t + 3));
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    lds_barrier();
+    lds_barrier();   // the P.V waves have waited for K of step t+1
   };
 
   if (n_steps > 0) {
@@ -474,37 +461,38 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
   }
 
-  // ---- segment partials: m is identical in every score wave; l sums the
-  // page slots' key subsets in a fixed order; the P.V waves then divide their
-  // accumulators by l and stage fp16 o in LDS for full-row stores.
-  __syncthreads();   // all transfers have landed; LDS is free
-  float* const lsum = (float*)smem;                     // [slot][row]
-  float* const mrow = lsum + kPagesPerStep * C::kRows;  // [row]
-  float* const ltot = mrow + C::kRows;                  // [row]
+  // ---- segment partials. The loop's last barrier has retired every LDS
+  // access and transfer. l of a row sums the page slots' key subsets in a
+  // fixed order (score and P.V waves alike); m is identical in every score
+  // wave. The P.V waves divide their accumulators by l and stage fp16 o in LDS
+  // for full-row stores.
+  float* const lsum = (float*)smem;   // [slot][row]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float l = l_lane[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (g == 0) lsum[w * C::kRows + 16 * rb + n] = l;
-    if (w == 0 && g == 0) mrow[16 * rb + n] = m_ref[rb];
   }
-  __syncthreads();
-  const int T = p.total_q, Hq = p.num_q_heads;
-  if (tid < rows) {
-    const int row = tid;
-    float l = lsum[row];
+  lds_barrier();   // row sums of every page slot
+  if (w == 0 && g == 0) {
+    const int T = p.total_q, Hq = p.num_q_heads;
 #pragma unroll
-    for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
-    ltot[row] = l;
-    const int i = row / G, gg = row - (row / G) * G;
-    float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
-    // streaming stores: the partials are read once, by the reduce
-    __builtin_nontemporal_store(mrow[row], dst);
-    __builtin_nontemporal_store(l, dst + 1);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int row = 16 * rb + n;
+      if (row < rows) {
+        float l = lsum[row];
+#pragma unroll
+        for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
+        const int i = row / G, gg = row - (row / G) * G;
+        float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
+        // streaming stores: the partials are read once, by the reduce
+        __builtin_nontemporal_store(m_ref[rb], dst);
+        __builtin_nontemporal_store(l, dst + 1);
+      }
+    }
   }
-  __syncthreads();   // l of every row visible to the P.V waves
-  __syncthreads();   // o staged
+  lds_barrier();   // o staged
   store_o<G>(p, geo, smem + C::kOffObuf);
 }
 
@@ -519,15 +507,25 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   const int lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int h = geo.h, q0 = geo.q0, L = geo.L, pb = geo.pb, pe = geo.pe;
   const int rows = geo.rows, n_steps = geo.n_steps;
-  uint8_t* const v_ring = smem + C::kOffStage + kStages * kStageBytes;
+  uint8_t* const k_ring = smem + C::kOffStage;
+  uint8_t* const v_ring = k_ring + kStages * kStageBytes;
 
-  PageStream vs;
+  // Both blocks of page slot v stream through this wave: K (page-id windows
+  // in the slot of score wave v, which streams nothing) three steps ahead of
+  // its use by the score waves, V three steps ahead of its use here.
+  PageStream ks, vs;
+  ks.init(p, geo, smem, v, v, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
   vs.init(p, geo, smem, w, v, lane, p.v_cache, lds_addr(v_ring), C::kOffIds);
   if (n_steps > 0) {
+    ks.fetch_window(0, lane);
     vs.fetch_window(0, lane);
-    const int id0 = vs.first_id(0);
+    const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
+    if (ks.has(0)) ks.put(0, id0);
+    if (ks.has(1)) ks.put(1, id1);
+    if (ks.has(2)) ks.put(2, id2);
     if (vs.has(0)) vs.put(0, id0);
-    wait_vm(vs.count(0));   // the window
+    wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // the windows and K of step 0
+    ks.next_id = ks.read_id(3);
     vs.next_id = vs.read_id(1);
   }
 
@@ -566,6 +564,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     const int u = t - 2;
     const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
     const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
+    ks.issue(t + 3, lane);
     vs.issue(t + 1, lane);
     unsigned flag_word = 0;
     if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
@@ -628,10 +627,12 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           for (int db = 0; db < 4; ++db)
             acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
     }
+    // K of step t+1 and V of step t-1 (issued in phase t-2) must have landed;
+    // the transfers of phases t-1 and t may fly
     if constexpr (kTail)
-      wait_vm(vs.count(t) + vs.count(t + 1));
+      wait_vm(ks.count(t + 2) + vs.count(t) + ks.count(t + 3) + vs.count(t + 1));
     else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     lds_barrier();
   };
 
@@ -648,10 +649,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
   }
 
-  __syncthreads();   // the score waves' epilogue: row sums, then l of every row
-  __syncthreads();
-  __syncthreads();
-  const float* const ltot = (const float*)smem + (kPagesPerStep + 1) * C::kRows;
+  lds_barrier();   // the score waves' row sums of every page slot
+  const float* const lsum = (const float*)smem;
   _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -659,13 +658,15 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rb + 4 * g + r;
       if (row < rows) {
-        const float l = ltot[row];
+        float l = lsum[row];
+#pragma unroll
+        for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
         const float inv = l > 0.f ? 1.0f / l : 0.f;   // no visible key: o = 0
 #pragma unroll
         for (int db = 0; db < 4; ++db) obuf[row * kHeadDim + kVDims * v + 16 * db + n] = (_Float16)(acc[rb][db][r] * inv);
       }
     }
-  __syncthreads();
+  lds_barrier();
   store_o<G>(p, geo, smem + C::kOffObuf);
 }
 
