@@ -40,6 +40,14 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   if (row >= rows_total) return;
   const int S = p.num_segments;
 
+  // the o loads of the first segments go out before (m, l) is known
+  const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
+  const int64_t seg_stride = rows_total * kHeadDim;
+  f16x4 a[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k)
+    if (k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + k * seg_stride));
+
   float m = -__builtin_inff(), l = 0.f;
   if (lane < S) {
     const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
@@ -55,13 +63,12 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   for (int k = 1; k < 64; k <<= 1) den += __shfl_xor(den, k, 64);
 
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
-  const int64_t seg_stride = rows_total * kHeadDim;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
-    f16x4 a[kBatch];
+    if (s0 > 0) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
+      for (int k = 0; k < kBatch; ++k)
+        if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
+    }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
       if (s0 + k < S) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
