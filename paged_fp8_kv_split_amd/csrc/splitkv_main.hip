@@ -235,6 +235,28 @@ struct PageStream {
       next_id = read_id(t + 1);
     }
   }
+  // The same transfer in four parts that the caller spreads over its work:
+  // begin() resolves the page (and refills the window when due), part(q, jj)
+  // moves the jj-th KiB.
+  struct Pending {
+    const uint8_t* base;
+    unsigned dst;
+    bool on;
+  };
+  __device__ Pending begin(int t, int lane) {
+    Pending q{nullptr, 0u, has(t)};
+    if (q.on) {
+      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
+      const int id = min(max(__builtin_amdgcn_readfirstlane(next_id), 0), num_pages - 1);
+      q.base = cache + (uint64_t)id * page_stride;
+      q.dst = ring + (t % kStages) * kStageBytes;
+      next_id = read_id(t + 1);
+    }
+    return q;
+  }
+  __device__ void part(const Pending& q, int jj) const {
+    if (q.on) dma_1k(q.base, goff[jj], q.dst + 1024 * jj);
+  }
 };
 
 // Stores the staged fp16 o rows ([row][256] in LDS) of the work-group's
@@ -564,8 +586,21 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     const int u = t - 2;
     const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
     const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
-    ks.issue(t + 3, lane);
-    vs.issue(t + 1, lane);
+    // K of step t+3 and V of step t+1: eight 1 KiB parts, spread over the
+    // MFMA groups below so that a part that waits for room in the memory
+    // pipeline does not hold up the whole phase's arithmetic
+    const PageStream::Pending kq = ks.begin(t + 3, lane);
+    const PageStream::Pending vq = vs.begin(t + 1, lane);
+    auto parts = [&](int d0, int d1) {
+      __builtin_amdgcn_sched_barrier(0);
+      for (int d = d0; d < d1; ++d) {
+        if (d < 4)
+          ks.part(kq, d);
+        else
+          vs.part(vq, d - 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
     unsigned flag_word = 0;
     if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
     // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
@@ -622,10 +657,15 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
           for (int db = 0; db < 4; ++db)
             acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
+          const int gi = kk * NRB + rb;
+          parts(8 * gi / (2 * NRB), 8 * (gi + 1) / (2 * NRB));
+        }
+    } else {
+      parts(0, 8);
     }
     // K of step t+1 and V of step t-1 (issued in phase t-2) must have landed;
     // the transfers of phases t-1 and t may fly
