@@ -11,10 +11,10 @@ query heads on 1 KV head, head_dim 256, fp8 e4m3 page-16 NHD K/V, 16 segments,
 16 replicas. Prints one JSON line on stdout; progress goes to stderr.
 
 The timed region is exactly --steps back-to-back calls between two HIP events on
-the launch stream, after --warmup untimed calls. A second, instrumented pass of
-the same length records events around every main-kernel launch to get that
-kernel's average duration for the roofline. The streaming-read ceiling and the
-CPU oracle (on a bounded sample) are measured in the same run.
+the launch stream, after --warmup untimed calls. A second pass of the same
+length launches only the main kernel, back to back between two HIP events on
+that stream, for its average duration in the roofline. The streaming-read
+ceiling and the CPU oracle (on a bounded sample) are measured in the same run.
 """
 
 import argparse
@@ -201,31 +201,21 @@ def main():
     log(f"{args.steps} calls: {us_per_call:.2f} us/call, {tbps:.3f} TB/s effective "
         f"(host {host_s * 1e6 / args.steps:.1f} us/call to enqueue)")
 
-    # ---- instrumented pass: events around each main-kernel launch
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # ---- main kernel alone: the same number of back-to-back main-kernel
+    # launches (same replica rotation) between two events on the launch stream
+    for k in range(min(args.warmup, 20)):
+        lib.pfkv_splitkv_main(refs[k % R], handle)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
     for k in range(args.steps):
-        starts[k].record(stream)
         st = lib.pfkv_splitkv_main(refs[k % R], handle)
-        ends[k].record(stream)
-        st |= lib.pfkv_segment_reduce(refs[k % R], handle)
         if st != 0:
             raise binding.PfkvError(st, binding.last_error())
+    m1.record(stream)
     torch.cuda.synchronize()
-    main_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) * 1e3 / args.steps
+    main_us = m0.elapsed_time(m1) * 1e3 / args.steps
     achieved_gbps = w.kv_bytes / (main_us * 1e-6) / 1e9
     log(f"main kernel alone: {main_us:.2f} us/launch, {achieved_gbps / 1e3:.3f} TB/s")
-
-    if args.copy_calibration:
-        # an elementwise kernel (not a DMA-engine memcpy), so counters see it as a dispatch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x elementwise copy of 1 GiB fp32 (reads 1 GiB, writes 1 GiB)")
-        del src, dst
-        torch.cuda.empty_cache()
 
     ceiling = None
     if not args.no_ceiling:
