@@ -86,7 +86,9 @@ int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
 /*
  * Enqueue the verify-attention call on `stream` (a hipStream_t; NULL = the null
  * stream): the split-KV main kernel on a grid of num_segments x num_seqs x
- * num_kv_heads work-groups, then the segment reduce. Validates with
+ * num_kv_heads work-groups, then the segment reduce. With num_segments == 1
+ * the main kernel writes out itself and no reduce is enqueued (the workspace is
+ * still validated but not touched). Validates with
  * pfkv_check_args against the current device first and checks that the device
  * pointers belong to it. Aliasing between out and any input is not allowed.
  * Concurrent calls that share a workspace race; give each stream its own.
@@ -99,7 +101,8 @@ int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);
  * pfkv_splitkv_main enqueues only the split-KV main kernel, which writes the
  * per-segment partials to the workspace; pfkv_segment_reduce enqueues only the
  * reduce that turns the workspace into out. Running them in this order on one
- * stream is exactly pfkv_verify_attn_fwd.
+ * stream is exactly pfkv_verify_attn_fwd. With num_segments == 1,
+ * pfkv_splitkv_main writes out directly and pfkv_segment_reduce enqueues nothing.
  */
 int pfkv_splitkv_main(const pfkv_args* args, void* stream);
 int pfkv_segment_reduce(const pfkv_args* args, void* stream);

@@ -220,6 +220,11 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.k_descale = a->k_descale;
   m.ws_o = ws_o;
   m.ws_ml = ws_ml;
+  m.out = (uint16_t*)a->out;
+  m.out_stride_token = a->out_stride_token;
+  m.out_stride_head = a->out_stride_head;
+  m.v_descale = a->v_descale;
+  m.direct = a->num_segments == 1 ? 1 : 0;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;
   m.num_q_heads = a->num_q_heads;
@@ -269,7 +274,7 @@ int pfkv_verify_attn_fwd(const pfkv_args* a, void* stream) {
   pfkv::ReduceParams rp;
   int st = prepare(a, &mp, &rp);
   if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
-  if (st == PFKV_OK) st = launch_reduce(rp, stream);
+  if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);   // one segment: out is final
   return st;
 }
 
@@ -285,7 +290,7 @@ int pfkv_segment_reduce(const pfkv_args* a, void* stream) {
   pfkv::MainParams mp;
   pfkv::ReduceParams rp;
   int st = prepare(a, &mp, &rp);
-  if (st == PFKV_OK) st = launch_reduce(rp, stream);
+  if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);
   return st;
 }
 

@@ -30,6 +30,11 @@ struct MainParams {
   const float* k_descale;
   uint16_t* ws_o;              // fp16 bits
   float* ws_ml;
+  // with a single segment the main kernel writes the bf16 output itself
+  uint16_t* out;               // bf16 bits
+  int64_t out_stride_token, out_stride_head;
+  const float* v_descale;
+  int32_t direct;              // num_segments == 1
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
 };
@@ -42,6 +47,13 @@ struct ReduceParams {
   int64_t out_stride_token, out_stride_head;
   int32_t total_q, num_q_heads, num_segments;
 };
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);

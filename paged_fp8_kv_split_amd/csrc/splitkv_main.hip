@@ -259,10 +259,21 @@ struct PageStream {
   }
 };
 
-// Stores the staged fp16 o rows ([row][256] in LDS) of the work-group's
-// segment with 16-byte streaming stores, all 512 threads.
+// Stores the staged 16-bit rows ([row][256] in LDS) of the work-group, all
+// 512 threads: fp16 o rows to the workspace with 16-byte streaming stores, or,
+// with a single segment, the final bf16 rows to out with 8-byte stores (out
+// rows are 8-byte aligned).
 template <int G>
-__device__ __forceinline__ void store_o(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
+__device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
+  if (p.direct) {
+    for (int idx = threadIdx.x; idx < geo.rows * 64; idx += kThreads) {
+      const int row = idx >> 6, c = idx & 63;
+      const int i = row / G, gg = row - (row / G) * G;
+      uint16_t* dst = p.out + (int64_t)(geo.q0 + i) * p.out_stride_token + (int64_t)(geo.h * G + gg) * p.out_stride_head + 4 * c;
+      *(uint2*)dst = *(const uint2*)(obuf + row * 512 + 8 * c);
+    }
+    return;
+  }
   const int T = p.total_q, Hq = p.num_q_heads;
   for (int idx = threadIdx.x; idx < geo.rows * 32; idx += kThreads) {
     const int row = idx >> 5, c = idx & 31;
@@ -497,7 +508,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     if (g == 0) lsum[w * C::kRows + 16 * rb + n] = l;
   }
   lds_barrier();   // row sums of every page slot
-  if (w == 0 && g == 0) {
+  if (w == 0 && g == 0 && !p.direct) {
     const int T = p.total_q, Hq = p.num_q_heads;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -515,7 +526,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
   }
   lds_barrier();   // o staged
-  store_o<G>(p, geo, smem + C::kOffObuf);
+  store_rows<G>(p, geo, smem + C::kOffObuf);
 }
 
 // P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
@@ -692,6 +703,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   lds_barrier();   // the score waves' row sums of every page slot
   const float* const lsum = (const float*)smem;
   _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
+  uint16_t* const obuf_bits = (uint16_t*)obuf;
+  const float vd = p.direct ? *(const const_f32*)p.v_descale : 1.f;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -701,13 +714,20 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         float l = lsum[row];
 #pragma unroll
         for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
-        const float inv = l > 0.f ? 1.0f / l : 0.f;   // no visible key: o = 0
+        // o = acc / l (0 with no visible key); a single segment writes out = vd o
+        const float inv = l > 0.f ? vd / l : 0.f;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) obuf[row * kHeadDim + kVDims * v + 16 * db + n] = (_Float16)(acc[rb][db][r] * inv);
+        for (int db = 0; db < 4; ++db) {
+          const int at = row * kHeadDim + kVDims * v + 16 * db + n;
+          if (p.direct)
+            obuf_bits[at] = (uint16_t)bf16_rne(acc[rb][db][r] * inv);
+          else
+            obuf[at] = (_Float16)(acc[rb][db][r] * inv);
+        }
       }
     }
   lds_barrier();
-  store_o<G>(p, geo, smem + C::kOffObuf);
+  store_rows<G>(p, geo, smem + C::kOffObuf);
 }
 
 template <int G, int NRB>

@@ -3,6 +3,7 @@
 Every call goes through the C ABI (ctypes binding) of the in-tree libpfkv.so.
 """
 
+import ctypes
 import math
 
 import numpy as np
@@ -175,21 +176,46 @@ def test_rerun_bitwise():
         assert torch.equal(a.view(torch.int16), o.view(torch.int16))
 
 
-@pytest.mark.parametrize("group", [16, 8])
-def test_short_qlen_rows_match_verify_bitwise(group):
-    """Draft-extend (q_len 1..3) and decode rows equal the verify call's rows bit for bit."""
+@pytest.mark.parametrize("group,segments", [(16, 8), (8, 8), (16, 1)])
+def test_short_qlen_rows_match_verify_bitwise(group, segments):
+    """Draft-extend (q_len 1..3) and decode rows equal the verify call's rows bit for bit
+    (with one segment, through the main kernel's direct bf16 output)."""
     w = Workload(name="v", ctx=(5000, 777, 40, 16), q_lens=(4, 4, 4, 4), num_q_heads=group, num_kv_heads=1,
-                 num_segments=8, seed=34)
+                 num_segments=segments, seed=34)
     case = make_case(w, "cpu").to(DEV)
-    verify = run(case, num_segments=8)
+    verify = run(case, num_segments=segments)
     for q_len in (1, 2, 3):
         rows = [4 * b + 4 - q_len + i for b in range(w.num_seqs) for i in range(q_len)]
         q = case.q[torch.tensor(rows, device=DEV)].contiguous()
         cu = torch.arange(0, q_len * (w.num_seqs + 1), q_len, dtype=torch.int32, device=DEV)
         short = pfkv.verify_attn(q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, cu,
-                                 case.k_descale, case.v_descale, case.softmax_scale, num_segments=8)
+                                 case.k_descale, case.v_descale, case.softmax_scale, num_segments=segments)
         torch.cuda.synchronize()
         assert torch.equal(short.view(torch.int16), verify[torch.tensor(rows, device=DEV)].view(torch.int16)), q_len
+
+
+def test_single_segment_writes_out_directly():
+    """With one segment the main kernel writes the bf16 output itself: the workspace stays
+    untouched, the reduce entry point enqueues nothing, and the result is the full call's."""
+    case = _case("multigroup")
+    T, Hq = case.q.shape[0], case.q.shape[1]
+    lib = pfkv.load_library()
+    stream = torch.cuda.current_stream()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    full = run(case, num_segments=1)
+    ws = torch.full((pfkv.workspace_bytes(1, T, Hq),), 0x5A, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(case.q, 7.0)
+    args = pfkv.binding.build_args(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                                   case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, 1, out, ws)
+    assert lib.pfkv_splitkv_main(ctypes.byref(args), handle) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), full.view(torch.int16))
+    assert bool((ws == 0x5A).all()), "the single-segment path must not touch the workspace"
+    out.fill_(7.0)
+    assert lib.pfkv_segment_reduce(ctypes.byref(args), handle) == 0
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "the reduce has nothing to do with one segment"
+    assert_parity(full, oracle_for(case), "multigroup S=1 direct")
 
 
 # ------------------------------------------------------------------ closed forms and edge cases
