@@ -35,6 +35,12 @@ HBM_PEAK_GBPS = 8000.0
 # i.e. 286.72 MB / 67 us = 4.28 TB/s under the same bytes / time formula.
 PAGES_TBPS = 286.72e6 / 67e-6 / 1e12
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "splitkv_main_prod_counters.json")
+# precision name -> (C ABI value, dtype text)
+PRECISIONS = {
+    "16bit": (0, "fp8-e4m3 K/V bytes; bf16 QK and fp16 PV MFMA, fp32 accumulate"),
+    "fp8p": (1, "fp8-e4m3 K/V bytes; bf16 QK MFMA, e4m3 P x e4m3 V on the fp8 MFMA, fp32 accumulate"),
+    "fp8": (2, "fp8-e4m3 K/V bytes; e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA, fp32 accumulate"),
+}
 
 
 def log(msg):
@@ -136,6 +142,8 @@ def main():
     ap.add_argument("--segments", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--precision", choices=list(PRECISIONS), default="16bit",
+                    help="arithmetic of the timed path (the others are timed too, as variants)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy 3 times, to scale HBM byte counters")
     args = ap.parse_args()
@@ -170,9 +178,12 @@ def main():
     T, Hq = w.total_q, w.num_q_heads
     out = torch.empty((T, Hq, w.head_dim), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device="cuda")
-    argv = [binding.build_args(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.cu_seqlens_q,
-                               c.k_descale, c.v_descale, c.softmax_scale, S, out, ws) for c in cases]
-    refs = [ctypes.byref(a) for a in argv]
+    def make_refs(prec):
+        argv = [binding.build_args(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.cu_seqlens_q,
+                                   c.k_descale, c.v_descale, c.softmax_scale, S, out, ws, prec) for c in cases]
+        return argv, [ctypes.byref(a) for a in argv]
+
+    argv, refs = make_refs(PRECISIONS[args.precision][0])
     stream = torch.cuda.current_stream()
     handle = ctypes.c_void_p(stream.cuda_stream)
 
@@ -217,6 +228,27 @@ def main():
     achieved_gbps = w.kv_bytes / (main_us * 1e-6) / 1e9
     log(f"main kernel alone: {main_us:.2f} us/launch, {achieved_gbps / 1e3:.3f} TB/s")
 
+    # ---- the other precisions, same protocol (reported as variants, not as value)
+    variants = {}
+    for other_name, (other, _) in PRECISIONS.items():
+        if other_name == args.precision:
+            continue
+        argv_o, refs_o = make_refs(other)
+        for k in range(args.warmup):
+            lib.pfkv_verify_attn_fwd(refs_o[k % R], handle)
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for k in range(args.steps):
+            st = lib.pfkv_verify_attn_fwd(refs_o[k % R], handle)
+            if st != 0:
+                raise binding.PfkvError(st, binding.last_error())
+        v1.record(stream)
+        torch.cuda.synchronize()
+        other_us = v0.elapsed_time(v1) * 1e3 / args.steps
+        variants[other_name] = {"us_per_call": round(other_us, 2),
+                                "value": round(w.kv_bytes / (other_us * 1e-6) / 1e12, 4)}
+        log(f"{other_name} variant: {other_us:.2f} us/call, {variants[other_name]['value']:.3f} TB/s")
+
     ceiling = None
     if not args.no_ceiling:
         del cases[1:]
@@ -244,7 +276,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tbps / PAGES_TBPS, 4) if w.name == "prod" else None,
-        "dtype": "fp8-e4m3 K/V bytes; bf16 QK and fp16 PV MFMA, fp32 accumulate",
+        "dtype": PRECISIONS[args.precision][1],
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.num_seqs} seqs x ctx {w.ctx[0] if len(set(w.ctx)) == 1 else list(w.ctx)}, "
@@ -271,6 +303,8 @@ def main():
         "frac_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBPS, 4),
         "pages_asm_TBps_same_formula": round(PAGES_TBPS, 3),
         "cpu_baseline": cpu,
+        "precision": args.precision,
+        "variants": variants,
     }
     print(json.dumps(result), flush=True)
 

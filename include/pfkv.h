@@ -69,7 +69,23 @@ typedef struct pfkv_args {
   int32_t max_pages_per_seq;   /* columns of block_tables that may be read */
   int32_t num_segments;        /* S in [1, 64] */
   float softmax_scale;         /* multiplies q . k (after descale); finite and > 0 */
+  int32_t precision;           /* PFKV_PRECISION_* below */
 } pfkv_args;
+
+/*
+ * Arithmetic of the main kernel.
+ * PFKV_PRECISION_16BIT (0, the default): Q in bf16 against K converted exactly
+ *   to bf16; P rounded once to fp16 against V converted exactly to fp16; fp32
+ *   accumulation.
+ * PFKV_PRECISION_FP8_P (1): scores as in the default; P rounded to e4m3 and
+ *   P V on the fp8 MFMA against the cached e4m3 V bytes.
+ * PFKV_PRECISION_FP8 (2): the pages' precision class (aiter PR #5190, Kernel
+ *   notes and Accuracy): each query row quantised to e4m3 with scale amax / 448
+ *   and both contractions on the fp8 MFMA.
+ * With e4m3 P, probabilities below 2^-10 of a row's reference maximum flush to
+ * zero (the underflow the aiter PR #7375 review thread works through).
+ */
+enum pfkv_precision { PFKV_PRECISION_16BIT = 0, PFKV_PRECISION_FP8_P = 1, PFKV_PRECISION_FP8 = 2 };
 
 /*
  * Pure host-side validation; reads no device memory and needs no GPU.

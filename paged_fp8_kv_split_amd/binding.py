@@ -64,6 +64,7 @@ class PfkvArgs(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_segments", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("precision", ctypes.c_int32),
     ]
 
 
@@ -145,8 +146,13 @@ def _as_bytes(cache: torch.Tensor) -> torch.Tensor:
     return cache
 
 
+PRECISION_16BIT = 0   # bf16 Q x exact-bf16 K, fp16 P x exact-fp16 V (default)
+PRECISION_FP8_P = 1   # scores as the default, e4m3 P x e4m3 V on the fp8 MFMA
+PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
+
+
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-               softmax_scale, num_segments_, out, workspace) -> PfkvArgs:
+               softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT) -> PfkvArgs:
     """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here)."""
     k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
@@ -196,14 +202,18 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.max_pages_per_seq = block_tables.shape[1]
     a.num_segments = int(num_segments_)
     a.softmax_scale = float(softmax_scale)
+    a.precision = int(precision)
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-                softmax_scale, num_segments=None, out=None, workspace=None, stream=None):
+                softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
+                precision=PRECISION_16BIT):
     """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``).
 
     ``num_segments=None`` picks the library heuristic from the device's CU count.
+    ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
+    ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
     ``workspace`` (uint8, at least :func:`workspace_bytes` bytes) is allocated with
     torch when not given. The call is enqueued on ``stream`` (default: torch's
     current stream) and does not synchronize.
@@ -220,7 +230,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
         need = workspace_bytes(num_segments, q.shape[0], q.shape[1])
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-                   softmax_scale, num_segments, out, workspace)
+                   softmax_scale, num_segments, out, workspace, precision)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

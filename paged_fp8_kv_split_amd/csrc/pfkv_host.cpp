@@ -124,6 +124,9 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
     return fail(PFKV_INVALID, "block_table_stride < max_pages_per_seq");
   if (a->num_segments < 1 || a->num_segments > pfkv::kMaxSegments)
     return fail(PFKV_INVALID, "num_segments must be in [1, 64]");
+  if (a->precision != PFKV_PRECISION_16BIT && a->precision != PFKV_PRECISION_FP8_P &&
+      a->precision != PFKV_PRECISION_FP8)
+    return fail(PFKV_INVALID, "precision must be one of PFKV_PRECISION_16BIT, _FP8_P, _FP8");
   if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
     return fail(PFKV_INVALID, "softmax_scale must be finite and positive");
   if (a->q_stride_token <= 0 || a->q_stride_head <= 0 || a->out_stride_token <= 0 || a->out_stride_head <= 0)
@@ -225,6 +228,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.out_stride_head = a->out_stride_head;
   m.v_descale = a->v_descale;
   m.direct = a->num_segments == 1 ? 1 : 0;
+  m.precision = a->precision;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;
   m.num_q_heads = a->num_q_heads;

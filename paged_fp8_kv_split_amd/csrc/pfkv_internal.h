@@ -35,6 +35,7 @@ struct MainParams {
   int64_t out_stride_token, out_stride_head;
   const float* v_descale;
   int32_t direct;              // num_segments == 1
+  int32_t precision;           // 0: 16-bit Q/P, 1: e4m3 P, 2: e4m3 Q (per-row scale) and P
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
 };

@@ -58,6 +58,9 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 typedef __attribute__((address_space(4))) const float const_f32;
@@ -71,6 +74,10 @@ constexpr int kStageBytes = kPagesPerStep * kPageBytes;       // K (or V) of one
 constexpr int kDmaPerWave = kPageBytes / 1024;         // 4 x 1 KiB per wave per step
 constexpr int kVDims = kHeadDim / kPagesPerStep;       // 64 output dims per P.V wave
 constexpr float kLazySlack = 8.0f;                     // log2 units
+// arithmetic modes (the C ABI's precision values)
+constexpr int kMode16 = 0;      // bf16 Q x bf16 K, fp16 P x fp16 V
+constexpr int kModeFp8P = 1;    // bf16 Q x bf16 K, e4m3 P x e4m3 V
+constexpr int kModeFp8QP = 2;   // e4m3 Q x e4m3 K, e4m3 P x e4m3 V
 
 template <int G>
 struct Cfg {
@@ -283,11 +290,26 @@ __device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, 
   }
 }
 
+// fp8 (e4m3fn) MFMA with unit block scales (E8M0 127 = 2^0) on both operands
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 // Score wave w (page slot w): K stream, S^T = K Q^T for all NRB row blocks,
-// lazy softmax, P to LDS, row sums; writes m and l of the segment.
-template <int G, int NRB>
+// lazy softmax, P to LDS, row sums; writes m and l of the segment. With F8,
+// Q is quantised per row to e4m3 (scale amax / 448, folded into that row's
+// score multiplier), S^T runs on the fp8 MFMA and P is rounded to e4m3.
+template <int G, int NRB, int MODE>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G>;
+  constexpr bool F8 = MODE == kModeFp8QP;    // e4m3 Q, S^T on the fp8 MFMA
+  constexpr bool F8P = MODE != kMode16;      // e4m3 P
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, g = lane >> 4, n = lane & 15;
@@ -320,10 +342,51 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   }
   // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
   // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
-  bf16x8 qop[NRB][4][2];
+  // With F8 (q8): byte b of k-step ks holds dim 128 ks + 32 g + b, and c2r is
+  // the row's score multiplier c2 * amax / 448.
+  bf16x8 qop[F8 ? 1 : NRB][4][2];
+  i32x8 q8[F8 ? NRB : 1][2];
+  float c2r[NRB], inv_c2r[NRB];
   auto load_q = [&]() {
+    if constexpr (F8) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int r = 16 * rb + n;
+        const bool pad = r >= rows;
+        bf16x8 x[2][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int pos = (16 * ks + 4 * g + c4) ^ n;
+            const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
+            x[ks][c4] = pad ? bf16x8{} : v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[ks][c4][e]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;   // q8 = e4m3(q * qs)
+        c2r[rb] = c2 / qs;
+        inv_c2r[rb] = 1.0f / c2r[rb];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            const bf16x8& xv = x[ks][d >> 1];
+            const int e = 4 * (d & 1);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e] * qs, (float)xv[e + 1] * qs, 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e + 2] * qs, (float)xv[e + 3] * qs, word, true);
+            q8[rb][ks][d] = word;
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
+      c2r[rb] = c2;
+      inv_c2r[rb] = 1.0f / c2;
       const int r = 16 * rb + n;
       const bool pad = r >= rows;
 #pragma unroll
@@ -338,21 +401,28 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   };
 
   // ---- per-lane LDS addresses
-  const unsigned kcol = 16u * ((g ^ n ^ (12 * (w & 1))) & 15);
+  // K of key n: bf16 path chunks 4u + g (u = 0..3); fp8 path chunks 2g, 2g+1
+  // (k-step 0) and 8 + 2g, 9 + 2g (k-step 1); a chunk c sits at c ^ sw
+  const unsigned ksw = (unsigned)((n ^ (12 * (w & 1))) & 15);
   unsigned k_off[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) k_off[u] = C::kOffStage + w * kPageBytes + 256 * n + (kcol ^ (64u * u));
+  for (int u = 0; u < 4; ++u) {
+    const unsigned c = F8 ? (unsigned)(2 * g + (u & 1) + 8 * (u >> 1)) : (unsigned)(4 * u + g);
+    k_off[u] = C::kOffStage + w * kPageBytes + 256 * n + 16u * (c ^ ksw);
+  }
   // P of row 16 rb + n, keys 4g..4g+3 of slot w: half (w & 1) of the 16-byte
   // A operand of lane (g, n) in k-step w >> 1
   const int p_off = C::kOffP + ((w >> 1) * 64 + lane) * 16 + (w & 1) * 8;
+  // fp8 P: row-major [row][64 keys], 16-key chunk (page slot) w of row r at
+  // position w ^ ((r >> 2) & 3); this lane writes keys 4g..4g+3
+  auto p8_off = [&](int rb) { const int r = 16 * rb + n; return C::kOffP + r * 64 + 16 * (w ^ ((r >> 2) & 3)) + 4 * g; };
   float* const mx = (float*)(smem + C::kOffMx);
   float* const alpha_buf = (float*)(smem + C::kOffAlpha);
 
   f32x4 sv[NRB];            // raw scores of the current step: lane (g, n) key 4g + r, row 16 rb + n
   float m_ref[NRB];         // reference max (log2 units) of row 16 rb + n, identical in every score wave
-  float thr[NRB];           // raw-score threshold (m + slack) / c2
+  float thr[NRB];           // raw-score threshold (m + slack) / c2r
   float l_lane[NRB];        // this lane's share of the row sums
-  const float inv_c2 = 1.0f / c2;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     m_ref[rb] = -__builtin_inff();
@@ -370,14 +440,23 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     if (!kTail || ks.has(t)) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) sv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F8) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 k0 = fp8x8_to_bf16(kraw[u][0], kraw[u][1]);
-        const bf16x8 k1 = fp8x8_to_bf16(kraw[u][2], kraw[u][3]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const i32x8 ka = cat8(kraw[2 * ks], kraw[2 * ks + 1]);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rb][u][0], sv[rb], 0, 0, 0);
-          sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[rb][u][1], sv[rb], 0, 0, 0);
+          for (int rb = 0; rb < NRB; ++rb) sv[rb] = mfma_fp8_16x16x128(ka, q8[rb][ks], sv[rb]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 k0 = fp8x8_to_bf16(kraw[u][0], kraw[u][1]);
+          const bf16x8 k1 = fp8x8_to_bf16(kraw[u][2], kraw[u][3]);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rb][u][0], sv[rb], 0, 0, 0);
+            sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[rb][u][1], sv[rb], 0, 0, 0);
+          }
         }
       }
       if (kTail && kPageSize * (pidx + 1) > L - q_len + 1) {
@@ -402,13 +481,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   // while the flag word (any score wave saw a row pass its threshold in step
   // u) is still in flight; in the rare slow path it is formed again.
   auto form_p = [&](int u, int pbuf, unsigned flag_word) {
-    f16x4 pv[NRB];
+    f32x4 pv[NRB];
     auto exps = [&]() {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[rb][r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2, -mref));
+        for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2r[rb], -mref));
       }
     };
     exps();
@@ -427,22 +506,36 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         float alpha = 1.f;
         if (M > thr[rb]) {
-          const float m_new = M * c2;
+          const float m_new = M * c2r[rb];
           alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);   // 0 when m was -inf
           m_ref[rb] = m_new;
-          thr[rb] = (m_new + kLazySlack) * inv_c2;
+          thr[rb] = (m_new + kLazySlack) * inv_c2r[rb];
         }
         l_lane[rb] *= alpha;
         if (w == 0 && g == 0) alpha_buf[(u & 1) * C::kRows + 16 * rb + n] = alpha;
       }
       exps();
     }
-    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    if constexpr (F8P) {
+      // e4m3 P (round to nearest even); l sums the rounded values
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = pv[rb];
-      const f16x2 lo = {pv[rb][0], pv[rb][1]}, hi = {pv[rb][2], pv[rb][3]};
-      l_lane[rb] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[rb], false), false);
+      for (int rb = 0; rb < NRB; ++rb) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][0], pv[rb][1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][2], pv[rb][3], word, true);
+        *(int*)(smem + p8_off(rb) + pbuf * C::kPBytes) = word;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+        l_lane[rb] += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
+    } else {
+      const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const f16x4 ph = {(_Float16)pv[rb][0], (_Float16)pv[rb][1], (_Float16)pv[rb][2], (_Float16)pv[rb][3]};
+        *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = ph;
+        const f16x2 lo = {ph[0], ph[1]}, hi = {ph[2], ph[3]};
+        l_lane[rb] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[rb], false), false);
+      }
     }
   };
 
@@ -530,10 +623,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 }
 
 // P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
-// NRB row blocks; stages its slice of the segment's normalised output o.
-template <int G, int NRB>
+// NRB row blocks; stages its slice of the segment's normalised output o. With
+// F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
+// e4m3 bytes.
+template <int G, int NRB, int MODE>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G>;
+  constexpr bool F8 = MODE != kMode16;       // e4m3 P and V on the fp8 MFMA
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int v = w - 4;
@@ -576,11 +672,45 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   const int p_off = C::kOffP + lane * 16;
   const float* const alpha_buf = (const float*)(smem + C::kOffAlpha);
 
-  f32x4 acc[NRB][4];
+  // fp8 path. Lane l of a 32x32x64 tile: A (P) row 32 rt + (l & 31) with keys
+  // 32 q .. 32 q + 31 (q = l >> 5) of the step as bytes 0..31; B (V) dim
+  // 32 dt + (l & 31) of this wave's 64 with the same keys, gathered by four
+  // ds_read_b64_tr_b8 of 8 keys each: in its 16-lane group, source lane
+  // 2k + hb supplies the 8 dims at +8 hb of key 32 q + 8 j + k.
+  constexpr int NRT = (NRB + 1) / 2;    // 32-row tiles
+  unsigned v8_off[F8 ? 2 : 1][4];
+  int p8_rd[F8 ? NRT : 1];
+  if constexpr (F8) {
+    const int q = lane >> 5, sub = (lane >> 4) & 1, src = lane & 15, kk8 = src >> 1, hb = src & 1;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) {
+        const int slot = 2 * q + (j >> 1), kin = 8 * (j & 1) + kk8;
+        const unsigned chunk = (unsigned)(4 * v + 2 * dt + sub);
+        const unsigned sw = (unsigned)((kin ^ (12 * (slot & 1))) & 15);
+        v8_off[dt][j] = C::kOffStage + kStages * kStageBytes + slot * kPageBytes + 256 * kin + 16u * (chunk ^ sw) + 8 * hb;
+      }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int r = 32 * rt + (lane & 31);
+      p8_rd[rt] = C::kOffP + r * 64 + 16 * ((2 * q) ^ ((r >> 2) & 3));   // chunk 2q; chunk 2q+1 at ^1
+    }
+  }
+
+  f32x4 acc[F8 ? 1 : NRB][4];
+  f32x16 acc8[F8 ? NRT : 1][2];
+  if constexpr (F8) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) acc8[rt][dt] = f32x16{};
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   bool slow1 = false;   // flag of step t-1 in phase t
   bool slow2 = false;   // flag of step t-2 in phase t
@@ -616,8 +746,21 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
     // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
     i32x2 vraw[2][4];
-    f16x8 pa[NRB][2];
-    if (have_pv) {
+    f16x8 pa[F8 ? 1 : NRB][2];
+    i32x8 pa8[F8 ? NRT : 1];
+    if (F8 && have_pv) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vraw[dt][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + v8_off[dt][j] + vst * kStageBytes));
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const uint8_t* pr = smem + p8_rd[rt] + pbuf * C::kPBytes;
+        pa8[rt] = cat8(*(const u32x4*)pr, *(const u32x4*)(smem + ((p8_rd[rt] + pbuf * C::kPBytes) ^ 16)));
+      }
+    }
+    if (!F8 && have_pv) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -633,7 +776,56 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     slow2 = slow1;
     slow1 = have_f && __builtin_amdgcn_readfirstlane(flag_word) != 0;
     if (slow1) lds_barrier();   // matches the score waves' maxima exchange
-    if (have_pv) {
+    if (F8 && have_pv) {
+      if constexpr (kTail) {
+        // keys past the segment or the sequence end: V bytes 0
+        if (u == n_steps - 1) {
+          const int q = lane >> 5;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int page = pb + kPagesPerStep * u + 2 * q + (j >> 1);
+            unsigned lo = 0, hi = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int key = kPageSize * page + 8 * (j & 1) + k;
+              const unsigned m8 = (page < pe && key < L) ? 0xffu : 0u;
+              if (k < 4) lo |= m8 << (8 * k); else hi |= m8 << (8 * (k - 4));
+            }
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+              vraw[dt][j][0] &= (int)lo;
+              vraw[dt][j][1] &= (int)hi;
+            }
+          }
+        }
+      }
+      if (slow2) {
+        // rows 32 rt + 8 c + 4 (lane >> 5) + e hold acc8[rt][dt][4 c + e]
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 32 * rt + 8 * c + 4 * (lane >> 5));
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc8[rt][dt][4 * c + e] *= a[e];
+          }
+      }
+      i32x8 vb[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        vb[dt] = i32x8{vraw[dt][0][0], vraw[dt][0][1], vraw[dt][1][0], vraw[dt][1][1],
+                       vraw[dt][2][0], vraw[dt][2][1], vraw[dt][3][0], vraw[dt][3][1]};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
+          const int gi = rt * 2 + dt;
+          parts(8 * gi / (2 * NRT), 8 * (gi + 1) / (2 * NRT));
+        }
+    } else if (!F8 && have_pv) {
       f16x8 vf[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -705,6 +897,28 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
   uint16_t* const obuf_bits = (uint16_t*)obuf;
   const float vd = p.direct ? *(const const_f32*)p.v_descale : 1.f;
+  if constexpr (F8) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < rows) {
+          float l = lsum[row];
+#pragma unroll
+          for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
+          const float inv = l > 0.f ? vd / l : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const int at = row * kHeadDim + kVDims * v + 32 * dt + (lane & 31);
+            if (p.direct)
+              obuf_bits[at] = (uint16_t)bf16_rne(acc8[rt][dt][r] * inv);
+            else
+              obuf[at] = (_Float16)(acc8[rt][dt][r] * inv);
+          }
+        }
+      }
+  } else {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -726,19 +940,20 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         }
       }
     }
+  }
   lds_barrier();
   store_rows<G>(p, geo, smem + C::kOffObuf);
 }
 
-template <int G, int NRB>
+template <int G, int NRB, int MODE>
 __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
   if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB>(p, geo, smem);
+    score_wave<G, NRB, MODE>(p, geo, smem);
   else
-    pv_wave<G, NRB>(p, geo, smem);
+    pv_wave<G, NRB, MODE>(p, geo, smem);
 }
 
-template <int G>
+template <int G, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
   using C = Cfg<G>;
@@ -769,16 +984,16 @@ splitkv_main_kernel(MainParams p) {
   const int nrb = (geo.rows + 15) >> 4;
   if constexpr (G == 16) {
     switch (nrb) {
-      case 1: verify_segment<16, 1>(p, geo, smem); break;
-      case 2: verify_segment<16, 2>(p, geo, smem); break;
-      case 3: verify_segment<16, 3>(p, geo, smem); break;
-      default: verify_segment<16, 4>(p, geo, smem); break;
+      case 1: verify_segment<16, 1, MODE>(p, geo, smem); break;
+      case 2: verify_segment<16, 2, MODE>(p, geo, smem); break;
+      case 3: verify_segment<16, 3, MODE>(p, geo, smem); break;
+      default: verify_segment<16, 4, MODE>(p, geo, smem); break;
     }
   } else {
     if (nrb == 1)
-      verify_segment<8, 1>(p, geo, smem);
+      verify_segment<8, 1, MODE>(p, geo, smem);
     else
-      verify_segment<8, 2>(p, geo, smem);
+      verify_segment<8, 2, MODE>(p, geo, smem);
   }
 }
 
@@ -786,10 +1001,23 @@ splitkv_main_kernel(MainParams p) {
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream) {
   const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads);
-  if (group == 16) {
-    hipLaunchKernelGGL(splitkv_main_kernel<16>, grid, dim3(kThreads), 0, stream, p);
-  } else if (group == 8) {
-    hipLaunchKernelGGL(splitkv_main_kernel<8>, grid, dim3(kThreads), 0, stream, p);
+  const int mode = p.precision;
+  if (group != 16 && group != 8) return hipErrorInvalidValue;
+  if (mode == kMode16) {
+    if (group == 16)
+      hipLaunchKernelGGL((splitkv_main_kernel<16, kMode16>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((splitkv_main_kernel<8, kMode16>), grid, dim3(kThreads), 0, stream, p);
+  } else if (mode == kModeFp8P) {
+    if (group == 16)
+      hipLaunchKernelGGL((splitkv_main_kernel<16, kModeFp8P>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((splitkv_main_kernel<8, kModeFp8P>), grid, dim3(kThreads), 0, stream, p);
+  } else if (mode == kModeFp8QP) {
+    if (group == 16)
+      hipLaunchKernelGGL((splitkv_main_kernel<16, kModeFp8QP>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((splitkv_main_kernel<8, kModeFp8QP>), grid, dim3(kThreads), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

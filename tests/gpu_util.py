@@ -7,15 +7,18 @@ import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Case
 
-# Tolerances in units of the oracle output's population std (16-bit P path).
+# Tolerances in units of the oracle output's population std: the 16-bit P path,
+# and the fp8 bar (aiter PR #5190, Accuracy: fp8 Q/P in 0.075-0.13 sigma).
 MAX_ERR_SIGMA = 0.15
 MEAN_ERR_SIGMA = 0.02
+FP8_MAX_ERR_SIGMA = 0.15
+FP8_MEAN_ERR_SIGMA = 0.03
 
 
-def run(case: Case, num_segments=None, out=None, workspace=None):
+def run(case: Case, num_segments=None, out=None, workspace=None, precision=0):
     return pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                             case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale,
-                            num_segments=num_segments, out=out, workspace=workspace)
+                            num_segments=num_segments, out=out, workspace=workspace, precision=precision)
 
 
 def error_stats(got: torch.Tensor, ref: np.ndarray):
@@ -26,10 +29,12 @@ def error_stats(got: torch.Tensor, ref: np.ndarray):
     return err.max() / sigma, err.mean() / sigma
 
 
-def assert_parity(got, ref, label=""):
+def assert_parity(got, ref, label="", bounds=None):
+    """bounds = (max, mean) in units of sigma; default: the 16-bit P bar."""
     mx, mean = error_stats(got, ref)
     print(f"[parity] {label}: max|err|/std={mx:.4f} mean|err|/std={mean:.5f}", flush=True)
-    assert mx <= MAX_ERR_SIGMA and mean <= MEAN_ERR_SIGMA, (label, mx, mean)
+    max_s, mean_s = bounds if bounds is not None else (MAX_ERR_SIGMA, MEAN_ERR_SIGMA)
+    assert mx <= max_s and mean <= mean_s, (label, mx, mean)
     return mx, mean
 
 

@@ -2,6 +2,7 @@
 
 import ctypes
 import os
+import subprocess
 import re
 
 import pytest
@@ -33,9 +34,21 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def test_struct_layout_matches_header():
-    # pointers (10 x 8) + int64/uint64 (6 x 8) + 9 int32 + 1 float
-    assert ctypes.sizeof(binding.PfkvArgs) == 10 * 8 + 6 * 8 + 10 * 4
+def test_struct_layout_matches_header(tmp_path):
+    """Every field of the ctypes mirror sits at the offset the C compiler gives it."""
+    fields = [f for f, _ in binding.PfkvArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"pfkv.h\"\nint main(void) {\n"
+                   f'  printf("%zu\\n", sizeof(pfkv_args));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(pfkv_args, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(binding.PfkvArgs)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(binding.PfkvArgs, f).offset == off, f
 
 
 def _valid_args(**over):
@@ -90,6 +103,10 @@ CASES = [
     ("page 32", dict(page_size=32), "gfx950", UNSUPPORTED),
     ("gqa 4", dict(num_q_heads=4, workspace_size=pfkv.workspace_bytes(16, 64, 4)), "gfx950", UNSUPPORTED),
     ("gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32)), "gfx950", UNSUPPORTED),
+    ("precision fp8 P", dict(precision=1), "gfx950", OK),
+    ("precision fp8 Q/P", dict(precision=2), "gfx950", OK),
+    ("precision 3", dict(precision=3), "gfx950", INVALID),
+    ("precision -1", dict(precision=-1), "gfx950", INVALID),
     ("mi300", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
     ("gfx9500 lookalike", {}, "gfx9500", UNSUPPORTED),
 ]
