@@ -249,6 +249,17 @@ def main():
                                 "value": round(w.kv_bytes / (other_us * 1e-6) / 1e12, 4)}
         log(f"{other_name} variant: {other_us:.2f} us/call, {variants[other_name]['value']:.3f} TB/s")
 
+    if args.copy_calibration:
+        # an elementwise kernel (not a DMA-engine memcpy), so counters see it as a dispatch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x elementwise copy of 1 GiB fp32 (reads 1 GiB, writes 1 GiB)")
+        del src, dst
+        torch.cuda.empty_cache()
+
     ceiling = None
     if not args.no_ceiling:
         del cases[1:]
