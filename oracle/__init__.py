@@ -13,8 +13,10 @@ draft extend and decode", Modifications): for every query token of every
 sequence, masked softmax attention over that sequence's paged KV cache, with
 K/V decoded from fp8 e4m3 bytes and multiplied by their per-tensor descales,
 queries attending under a bottom-right causal mask to the last q_len positions,
-and G query heads sharing one KV head. Split-KV segmentation is an exact rewrite
-of this quantity, so the oracle does not depend on the segment count.
+and G query heads sharing one KV head; optionally the log-sum-exp of each row's
+visible scores (aiter PR #7375 "gfx1250 fp8 varlen FMHA", Summary). Split-KV
+segmentation is an exact rewrite of these quantities, so the oracle does not
+depend on the segment count.
 
 Every function here is pinned by ``tests/test_oracle.py`` to something other
 than itself (a library routine, brute force, closed forms, invariants, and the
@@ -24,6 +26,7 @@ value printed for the fp8 probability-underflow example on aiter PR #7375).
 from .attention import (  # noqa: F401
     E4M3FN_MAX,
     attend,
+    attend_lse,
     bf16_bits_to_f64,
     e4m3fn_decode_table,
     segment_page_ranges,

@@ -26,6 +26,7 @@ problem, with no blocking, fusion or reordering beyond it:
    positions"; SGLang PR #37465, Modifications: q_len 1 to 4 per sequence).
 6. Softmax over the visible keys with exact ``exp`` in fp64, then the weighted
    sum of V rows. A query with no visible key yields zeros.
+7. The optional log-sum-exp of the same scores (:func:`attend_lse`).
 """
 
 from __future__ import annotations
@@ -135,6 +136,48 @@ def attend(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
                 weights = np.exp(scores - top)
                 out[q0 + i, heads, :] = (weights @ vals[:vis, h, :]) / weights.sum(axis=1, keepdims=True)
     return out
+
+
+def attend_lse(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
+               k_descale, v_descale, softmax_scale) -> np.ndarray:
+    """Exact log-sum-exp of each row's visible scores; returns float64 ``[T, Hq]``.
+
+    lse[t, h] = ln sum_j exp(score_j) over the keys row (t, h) may see, with the
+    scores of :func:`attend` (steps 1-5 above); a row with no visible key gets
+    -inf (aiter PR #7375: the optional LSE of a varlen attention call, with
+    -inf for rows that have no finite value). Evaluated as top + ln sum_j
+    exp(score_j - top) so that no exp overflows. ``v_cache`` and ``v_descale``
+    do not enter; they are accepted so that the call matches :func:`attend`.
+    """
+    table = e4m3fn_decode_table()
+    qf = _queries_f64(q)
+    k_cache = np.asarray(k_cache, dtype=np.uint8)
+    seq_lens = np.asarray(seq_lens)
+    cu = np.asarray(cu_seqlens_q)
+    kd = float(np.float32(k_descale))
+    scale = float(np.float32(softmax_scale))
+
+    total_q, num_q_heads, _ = qf.shape
+    num_kv_heads = k_cache.shape[2]
+    group = num_q_heads // num_kv_heads
+    lse = np.full((total_q, num_q_heads), -np.inf)
+
+    for b in range(len(seq_lens)):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        q_len, seq_len = q1 - q0, int(seq_lens[b])
+        if q_len <= 0 or seq_len <= 0:
+            continue
+        keys = _gather_sequence(table, k_cache, block_tables[b], seq_len, kd)
+        for h in range(num_kv_heads):
+            heads = slice(h * group, (h + 1) * group)
+            for i in range(q_len):
+                vis = visible_key_count(seq_len, q_len, i)
+                if vis == 0:
+                    continue
+                scores = (qf[q0 + i, heads, :] @ keys[:vis, h, :].T) * scale  # [G, vis]
+                top = scores.max(axis=1)
+                lse[q0 + i, heads] = top + np.log(np.exp(scores - top[:, None]).sum(axis=1))
+    return lse
 
 
 def segment_page_ranges(n_pages: int, num_segments: int):

@@ -102,6 +102,33 @@ def _brute_force(case):
     return out
 
 
+def _brute_force_lse(case):
+    """ln sum exp(score) per (token, head) in pure Python (math.fsum), -inf without a visible key."""
+    a = case.host_arrays()
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()
+    q = case.q.to(torch.float64).numpy()
+    kc, bt = a["k_cache"], a["block_tables"]
+    page, hkv, d = kc.shape[1], kc.shape[2], kc.shape[3]
+    hq = q.shape[1]
+    kd, sc = float(np.float32(a["k_descale"])), float(np.float32(a["softmax_scale"]))
+    lse = np.full(q.shape[:2], -math.inf)
+    cu = a["cu_seqlens_q"]
+    for b, seq_len in enumerate(a["seq_lens"]):
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t = int(cu[b]) + i
+            for head in range(hq):
+                kvh = head // (hq // hkv)
+                scores = []
+                for j in range(min(int(seq_len), int(seq_len) - n + i + 1)):
+                    pg, slot = int(bt[b][j // page]), j % page
+                    scores.append(math.fsum(q[t, head, e] * dec[kc[pg, slot, kvh, e]] * kd for e in range(d)) * sc)
+                if scores:
+                    top = max(scores)
+                    lse[t, head] = top + math.log(math.fsum(math.exp(x - top) for x in scores))
+    return lse
+
+
 BRUTE_CASES = [
     dict(ctx=[13], q_lens=[4], hq=2, hkv=1),
     dict(ctx=[1, 7, 40], q_lens=[1, 3, 4], hq=4, hkv=2),
@@ -117,6 +144,45 @@ def test_oracle_matches_brute_force(cfg):
     got = _run_oracle(case)
     ref = _brute_force(case)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("cfg", BRUTE_CASES, ids=[str(i) for i in range(len(BRUTE_CASES))])
+def test_oracle_lse_matches_brute_force(cfg):
+    case = _tiny(seed=13, **cfg)
+    got = oracle.attend_lse(**case.host_arrays())
+    ref = _brute_force_lse(case)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_oracle_lse_closed_forms():
+    """One visible key: lse is its score. n identical visible keys: ln n + score."""
+    d = 8
+    k_codes = np.full((5, 1, d), 0x38, np.uint8)            # e4m3fn 0x38 = 1.0
+    v_codes = np.zeros_like(k_codes)
+    q_vals = np.array([[[0.5] * d], [[1.0] * d], [[-2.0] * d], [[0.25] * d]], np.float64)   # [4, 1, d]
+    prob = _single_page_problem(k_codes, v_codes, q_vals, q_len=4, kd=0.5, scale=0.25)
+    lse = oracle.attend_lse(**prob)
+    for i in range(4):
+        n_vis = 5 - 4 + i + 1
+        score = 0.25 * float(q_vals[i, 0, 0]) * 0.5 * d
+        assert lse[i, 0] == pytest.approx(math.log(n_vis) + score, rel=1e-14, abs=1e-14)
+    one = _single_page_problem(k_codes[:1], v_codes[:1], q_vals[:1], q_len=1, kd=0.5, scale=0.25)
+    assert oracle.attend_lse(**one)[0, 0] == pytest.approx(0.25 * 0.5 * 0.5 * d, rel=1e-15)
+
+
+@pytest.mark.parametrize("num_segments", [1, 3, 16])
+def test_oracle_lse_is_the_merge_of_segment_statistics(num_segments):
+    """ln sum_s 2^(lse2_s) over the segments' own statistics equals the whole row's lse."""
+    case = _tiny([70, 33, 5], [4, 2, 1], 4, 1, d=16, page=4, seed=21)
+    a = case.host_arrays()
+    lse2, _ = oracle.segment_partials(**a, num_segments=num_segments)
+    merged = np.logaddexp.reduce(lse2 * math.log(2.0), axis=0)
+    ref = oracle.attend_lse(**a)
+    assert np.array_equal(np.isinf(merged), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(merged[fin], ref[fin], rtol=1e-12, atol=1e-12)
 
 
 # ---------------------------------------------------------------- library special case
@@ -327,6 +393,18 @@ def _mutations():
         "page_slot_swap": ("_gather_sequence",
                            lambda t, c, row, L, ds: good_gather(t, c[:, ::-1], row, L, ds)),
     }
+
+
+@pytest.mark.parametrize("name", ["mask_off_by_one", "mask_top_left", "subnormal_exponent", "dropped_sign",
+                                  "dropped_descale", "page_slot_swap"])
+def test_planted_mistake_is_caught_in_lse(monkeypatch, name):
+    attr, bad = _mutations()[name]
+    case = _tiny([21, 6], [4, 3], 4, 2, d=8, page=4, seed=12, descale="fixed")
+    ref = _brute_force_lse(case)
+    monkeypatch.setattr(oracle_attention, attr, bad)
+    got = oracle_attention.attend_lse(**case.host_arrays())
+    fin = np.isfinite(ref) & np.isfinite(got)
+    assert not (np.array_equal(np.isinf(got), np.isinf(ref)) and np.allclose(got[fin], ref[fin], rtol=1e-6, atol=1e-9))
 
 
 @pytest.mark.parametrize("name", sorted(_mutations()))
