@@ -70,7 +70,24 @@ typedef struct pfkv_args {
   int32_t num_segments;        /* S in [1, 64] */
   float softmax_scale;         /* multiplies q . k (after descale); finite and > 0 */
   int32_t precision;           /* PFKV_PRECISION_* below */
+  float* lse;                  /* optional, NULL = not written: fp32 [num_q_heads, total_q], element (h, t)
+                                  at lse[h * total_q + t], 4-B aligned; see below */
 } pfkv_args;
+
+/*
+ * Log-sum-exp output (aiter PR #7375, Summary and Behavior and intent: an
+ * optional LSE in the varlen layout (heads, total tokens), computed from the
+ * same rounded softmax weights that normalise the output, so that output and
+ * LSE stay consistent for a later log-sum-exp merge of partial attentions).
+ * lse[h][t] = ln sum_j exp(softmax_scale * <q_t,h , k_j>) over the keys j the
+ * row may see (K descaled), where each exp is the probability the kernel
+ * weighted V with: p_j = 2^(c s_j - m) rounded as P is rounded (fp16, or e4m3
+ * for the fp8 P variants), so lse = ln 2 * (m + log2 sum_j p_j). It differs
+ * from the exact value by the relative rounding of P (at most 2^-11 with fp16
+ * P, i.e. 5e-4 in lse). A row with no visible key gets -inf (aiter PR #7375,
+ * review thread: non-finite reference rows are -inf). Written by the segment
+ * reduce, or by the main kernel when num_segments == 1.
+ */
 
 /*
  * Arithmetic of the main kernel.

@@ -65,6 +65,7 @@ class PfkvArgs(ctypes.Structure):
         ("num_segments", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("precision", ctypes.c_int32),
+        ("lse", ctypes.c_void_p),
     ]
 
 
@@ -152,8 +153,11 @@ PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
 
 
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-               softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT) -> PfkvArgs:
-    """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here)."""
+               softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None) -> PfkvArgs:
+    """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here).
+
+    ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device.
+    """
     k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
         raise TypeError("q must be bf16 [T, Hq, D] with unit last stride")
@@ -182,6 +186,11 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
             raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous uint8 tensor")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
+            raise TypeError("lse must be a contiguous float32 [Hq, T] tensor")
+        if lse.device != q.device:
+            raise ValueError(f"lse must be on q's device ({q.device}), got {lse.device}")
     a = PfkvArgs()
     a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
     a.block_tables, a.seq_lens, a.cu_seqlens_q = (block_tables.data_ptr(), seq_lens.data_ptr(),
@@ -203,14 +212,18 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.num_segments = int(num_segments_)
     a.softmax_scale = float(softmax_scale)
     a.precision = int(precision)
+    a.lse = lse.data_ptr() if lse is not None else None
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                 softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
-                precision=PRECISION_16BIT):
-    """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``).
+                precision=PRECISION_16BIT, return_lse=False, lse=None):
+    """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``), or
+    ``(out, lse)`` when ``return_lse`` is set or an ``lse`` buffer is given.
 
+    ``lse`` is float32 ``[Hq, T]``: the natural-log sum of exp(scores) over each
+    row's visible keys, -inf for a row without one (``include/pfkv.h``).
     ``num_segments=None`` picks the library heuristic from the device's CU count.
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
@@ -229,13 +242,15 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     if workspace is None:
         need = workspace_bytes(num_segments, q.shape[0], q.shape[1])
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-                   softmax_scale, num_segments, out, workspace, precision)
+                   softmax_scale, num_segments, out, workspace, precision, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     _raise_on(lib.pfkv_verify_attn_fwd(ctypes.byref(a), ctypes.c_void_p(handle)))
-    return out
+    return (out, lse) if lse is not None else out
 
 
 def num_segments_for(num_cus: int, num_seqs: int, num_kv_heads: int) -> int:

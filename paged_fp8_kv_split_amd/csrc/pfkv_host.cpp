@@ -146,7 +146,7 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (!aligned(a->k_cache, 16) || !aligned(a->v_cache, 16))
     return fail(PFKV_INVALID, "k_cache / v_cache must be 16-byte aligned");
   if (!aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4) || !aligned(a->cu_seqlens_q, 4) ||
-      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4))
+      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4) || !aligned(a->lse, 4))
     return fail(PFKV_INVALID, "int32 / fp32 arguments must be 4-byte aligned");
   const uint64_t need = pfkv_workspace_bytes(a->num_segments, a->total_q, a->num_q_heads);
   if (a->workspace_size < need)
@@ -202,6 +202,10 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
     st = check_device_pointer(x.p, device, x.name);
     if (st != PFKV_OK) return st;
   }
+  if (a->lse != nullptr) {
+    st = check_device_pointer(a->lse, device, "lse");
+    if (st != PFKV_OK) return st;
+  }
 
   const int group = a->num_q_heads / a->num_kv_heads;
   const uint64_t part_rows = (uint64_t)a->num_segments * a->total_q * a->num_q_heads;
@@ -227,6 +231,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.out_stride_token = a->out_stride_token;
   m.out_stride_head = a->out_stride_head;
   m.v_descale = a->v_descale;
+  m.lse = a->lse;
   m.direct = a->num_segments == 1 ? 1 : 0;
   m.precision = a->precision;
   m.num_seqs = a->num_seqs;
@@ -244,6 +249,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   rp->out = (uint16_t*)a->out;
   rp->out_stride_token = a->out_stride_token;
   rp->out_stride_head = a->out_stride_head;
+  rp->lse = a->lse;
   rp->total_q = a->total_q;
   rp->num_q_heads = a->num_q_heads;
   rp->num_segments = a->num_segments;

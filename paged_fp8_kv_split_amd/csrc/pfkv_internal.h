@@ -34,6 +34,7 @@ struct MainParams {
   uint16_t* out;               // bf16 bits
   int64_t out_stride_token, out_stride_head;
   const float* v_descale;
+  float* lse;                  // optional [Hq][T] fp32, written here when direct
   int32_t direct;              // num_segments == 1
   int32_t precision;           // 0: 16-bit Q/P, 1: e4m3 P, 2: e4m3 Q (per-row scale) and P
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
@@ -46,6 +47,7 @@ struct ReduceParams {
   const float* v_descale;
   uint16_t* out;               // bf16 bits
   int64_t out_stride_token, out_stride_head;
+  float* lse;                  // optional [Hq][T] fp32
   int32_t total_q, num_q_heads, num_segments;
 };
 

@@ -8,6 +8,9 @@
 //   out = v_descale * sum_s c_s o_s / sum_s c_s   (0 when the sum is 0),
 // then rounded to bf16 to nearest even. The numerator is summed in the order
 // s = 0, 1, ...; the denominator by a fixed butterfly over the wave's lanes.
+// With an lse buffer the row's log-sum-exp ln 2 (M + log2 sum_s c_s) goes to
+// lse[hq][t] (-inf when the sum is 0), the merge rule of split softmax
+// statistics (aiter PR #7375, Behavior and intent).
 // One wave per output row: lane s holds (m_s, l_s), every lane four dims of
 // the fp16 o rows, whose loads for up to 16 segments are in flight together.
 #include "pfkv_internal.h"
@@ -74,6 +77,8 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   const uint32_t lo = bf16_rne(num[0] * inv) | (bf16_rne(num[1] * inv) << 16);
   const uint32_t hi = bf16_rne(num[2] * inv) | (bf16_rne(num[3] * inv) << 16);
   *(uint2*)dst = make_uint2(lo, hi);
+  if (p.lse != nullptr && lane == 0)
+    p.lse[hq * p.total_q + t] = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 }  // namespace

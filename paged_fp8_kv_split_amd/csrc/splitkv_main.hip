@@ -601,7 +601,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     if (g == 0) lsum[w * C::kRows + 16 * rb + n] = l;
   }
   lds_barrier();   // row sums of every page slot
-  if (w == 0 && g == 0 && !p.direct) {
+  if (w == 0 && g == 0 && (!p.direct || p.lse != nullptr)) {
     const int T = p.total_q, Hq = p.num_q_heads;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -611,10 +611,16 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 #pragma unroll
         for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
         const int i = row / G, gg = row - (row / G) * G;
-        float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
-        // streaming stores: the partials are read once, by the reduce
-        __builtin_nontemporal_store(m_ref[rb], dst);
-        __builtin_nontemporal_store(l, dst + 1);
+        if (p.direct) {
+          // one segment: the row's log-sum-exp goes straight to lse (natural log)
+          p.lse[(int64_t)(h * G + gg) * T + q0 + i] =
+              l > 0.f ? (m_ref[rb] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -__builtin_inff();
+        } else {
+          float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
+          // streaming stores: the partials are read once, by the reduce
+          __builtin_nontemporal_store(m_ref[rb], dst);
+          __builtin_nontemporal_store(l, dst + 1);
+        }
       }
     }
   }

@@ -106,6 +106,8 @@ CASES = [
     ("precision fp8 P", dict(precision=1), "gfx950", OK),
     ("precision fp8 Q/P", dict(precision=2), "gfx950", OK),
     ("precision 3", dict(precision=3), "gfx950", INVALID),
+    ("lse given", dict(lse=0x1c0000), "gfx950", OK),
+    ("lse misaligned", dict(lse=0x1c0002), "gfx950", INVALID),
     ("precision -1", dict(precision=-1), "gfx950", INVALID),
     ("mi300", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
     ("gfx9500 lookalike", {}, "gfx9500", UNSUPPORTED),
