@@ -11,7 +11,10 @@
  * positions 0 .. L_b - n_b + i (a causal mask over the last n_b positions). The
  * cache is NHD with 16-token pages and head_dim 256; K and V are e4m3fn bytes
  * whose real values are byte * k_descale (resp. v_descale); G = Hq / Hkv query
- * heads (16 or 8) share each KV head, query head hq reading KV head hq / G. The
+ * heads share each KV head, query head hq reading KV head hq / G. The pages'
+ * kernel serves G = 16 and 8 (aiter PR #5190, Supported); this library also
+ * serves G = 4, and G = 32 as two work-groups of 16 query heads per KV head
+ * (each reads the KV head's pages, so G = 32 moves twice the K/V bytes). The
  * context of each sequence is cut into num_segments KV segments processed
  * independently; each writes partial softmax statistics to the workspace and a
  * second kernel merges them by log-sum-exp into the bf16 output.
@@ -119,7 +122,7 @@ int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
 /*
  * Enqueue the verify-attention call on `stream` (a hipStream_t; NULL = the null
  * stream): the split-KV main kernel on a grid of num_segments x num_seqs x
- * num_kv_heads work-groups, then the segment reduce. With num_segments == 1
+ * num_kv_heads work-groups (x 2 when G = 32), then the segment reduce. With num_segments == 1
  * the main kernel writes out itself and no reduce is enqueued (the workspace is
  * still validated but not touched). Validates with
  * pfkv_check_args against the current device first and checks that the device

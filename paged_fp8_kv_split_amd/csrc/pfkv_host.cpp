@@ -5,9 +5,10 @@
 // mtp_verify_attn_num_segments() of aiter PR #5190 ("gfx950 assembly MTP-verify
 // attention for head_dim 256 fp8 paged KV"), section Modifications; what is
 // accepted follows its section Supported (gfx950, head_dim 256, page 16, e4m3
-// per-tensor K/V, bf16 Q, GQA 16 or 8) with q_len 1..4 per sequence as in SGLang
-// PR #37465, Modifications. Unsupported shapes return PFKV_UNSUPPORTED so that a
-// caller can fall back, as the SGLang entry points do.
+// per-tensor K/V, bf16 Q, GQA 16 or 8; this library adds GQA 4 and 32) with
+// q_len 1..4 per sequence as in SGLang PR #37465, Modifications. Unsupported
+// shapes return PFKV_UNSUPPORTED so that a caller can fall back, as the SGLang
+// entry points do.
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -158,8 +159,8 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (a->head_dim != pfkv::kHeadDim) return fail(PFKV_UNSUPPORTED, "head_dim must be 256");
   if (a->page_size != pfkv::kPageSize) return fail(PFKV_UNSUPPORTED, "page_size must be 16");
   const int group = a->num_q_heads / a->num_kv_heads;
-  if (group != 16 && group != 8)
-    return fail(PFKV_UNSUPPORTED, "query heads per KV head must be 16 or 8, got " + std::to_string(group));
+  if (group != 32 && group != 16 && group != 8 && group != 4)
+    return fail(PFKV_UNSUPPORTED, "query heads per KV head must be 32, 16, 8 or 4, got " + std::to_string(group));
   return PFKV_OK;
 }
 
@@ -233,6 +234,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.v_descale = a->v_descale;
   m.lse = a->lse;
   m.direct = a->num_segments == 1 ? 1 : 0;
+  m.kv_split = group == 32 ? 2 : 1;
   m.precision = a->precision;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;
@@ -258,7 +260,8 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
 }
 
 int launch_main(const pfkv::MainParams& mp, int group, void* stream) {
-  const hipError_t e = pfkv::launch_splitkv_main(mp, group, (hipStream_t)stream);
+  // 32 query heads per KV head: two work-groups of 16 per KV head (mp.kv_split)
+  const hipError_t e = pfkv::launch_splitkv_main(mp, group == 32 ? 16 : group, (hipStream_t)stream);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PFKV_LAUNCH, std::string("split-KV main kernel launch: ") + hipGetErrorString(e));

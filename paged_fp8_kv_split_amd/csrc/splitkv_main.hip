@@ -81,7 +81,9 @@ constexpr int kModeFp8QP = 2;   // e4m3 Q x e4m3 K, e4m3 P x e4m3 V
 
 template <int G>
 struct Cfg {
-  static constexpr int kRowBlocks = G * kMaxQLen / 16;            // 16-row MFMA blocks (all rows)
+  // 16-row MFMA blocks (all rows); at least two, so that the 32-row tiles of
+  // the fp8 P.V path stay inside the P, maximum and rescale buffers
+  static constexpr int kRowBlocks = G * kMaxQLen / 16 < 2 ? 2 : G * kMaxQLen / 16;
   static constexpr int kRows = kRowBlocks * 16;
   static constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;         // fp16 P of a step: [rb][k-step][lane] x 16 B
   static constexpr int kOffP = 0;                                  // two P buffers
@@ -173,7 +175,8 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(unsigned lo, unsigned hi) {
 
 // Geometry of one work-group's (segment, sequence, KV head), uniform.
 struct Geo {
-  int seg, b, h;
+  int seg, b, h;     // h: this work-group's group of G query heads (query heads h G .. h G + G - 1)
+  int hkv;           // the KV head those query heads read
   int q0, q_len, L, pb, pe, rows, n_steps;
   float c2;          // k_descale * softmax_scale * log2(e): raw score -> log2 units
 };
@@ -208,7 +211,7 @@ struct PageStream {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int k = 4 * jj + g;
-      goff[jj] = (unsigned)((k * p.num_kv_heads + geo.h) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
+      goff[jj] = (unsigned)((k * p.num_kv_heads + geo.hkv) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
     }
     ring = ring_stage0 + slot * kPageBytes;
     ids_lds = lds_addr(smem + off_ids) + wave * (2 * 64 * 4);
@@ -971,6 +974,7 @@ splitkv_main_kernel(MainParams p) {
   geo.seg = blockIdx.x;
   geo.b = blockIdx.y;
   geo.h = blockIdx.z;
+  geo.hkv = blockIdx.z / p.kv_split;
   // out-of-contract values are clamped so that every access stays in its buffer
   geo.q0 = cu[geo.b];
   int q_len = cu[geo.b + 1] - geo.q0;
@@ -995,39 +999,42 @@ splitkv_main_kernel(MainParams p) {
       case 3: verify_segment<16, 3, MODE>(p, geo, smem); break;
       default: verify_segment<16, 4, MODE>(p, geo, smem); break;
     }
-  } else {
+  } else if constexpr (G == 8) {
     if (nrb == 1)
       verify_segment<8, 1, MODE>(p, geo, smem);
     else
       verify_segment<8, 2, MODE>(p, geo, smem);
+  } else {
+    verify_segment<4, 1, MODE>(p, geo, smem);
   }
+}
+
+// group: query heads per work-group (16, 8 or 4; 32 query heads per KV head run
+// as two 16-head work-groups, p.kv_split = 2)
+template <int MODE>
+hipError_t launch_mode(const MainParams& p, int group, hipStream_t stream) {
+  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split);
+  if (group == 16)
+    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE>), grid, dim3(kThreads), 0, stream, p);
+  else if (group == 8)
+    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE>), grid, dim3(kThreads), 0, stream, p);
+  else if (group == 4)
+    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE>), grid, dim3(kThreads), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream) {
-  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads);
-  const int mode = p.precision;
-  if (group != 16 && group != 8) return hipErrorInvalidValue;
-  if (mode == kMode16) {
-    if (group == 16)
-      hipLaunchKernelGGL((splitkv_main_kernel<16, kMode16>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((splitkv_main_kernel<8, kMode16>), grid, dim3(kThreads), 0, stream, p);
-  } else if (mode == kModeFp8P) {
-    if (group == 16)
-      hipLaunchKernelGGL((splitkv_main_kernel<16, kModeFp8P>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((splitkv_main_kernel<8, kModeFp8P>), grid, dim3(kThreads), 0, stream, p);
-  } else if (mode == kModeFp8QP) {
-    if (group == 16)
-      hipLaunchKernelGGL((splitkv_main_kernel<16, kModeFp8QP>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((splitkv_main_kernel<8, kModeFp8QP>), grid, dim3(kThreads), 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;
+  if (p.kv_split != 1 && !(p.kv_split == 2 && group == 16)) return hipErrorInvalidValue;
+  switch (p.precision) {
+    case kMode16: return launch_mode<kMode16>(p, group, stream);
+    case kModeFp8P: return launch_mode<kModeFp8P>(p, group, stream);
+    case kModeFp8QP: return launch_mode<kModeFp8QP>(p, group, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pfkv

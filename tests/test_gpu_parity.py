@@ -319,7 +319,7 @@ def test_strided_q_and_out():
 
 
 def test_unsupported_group_is_refused():
-    w = Workload(name="u", ctx=(64,), q_lens=(4,), num_q_heads=4, num_kv_heads=1, num_segments=1, seed=1)
+    w = Workload(name="u", ctx=(64,), q_lens=(4,), num_q_heads=2, num_kv_heads=1, num_segments=1, seed=1)
     case = make_case(w, "cpu").to(DEV)
     with pytest.raises(pfkv.PfkvError) as info:
         run(case, num_segments=1)

@@ -101,8 +101,10 @@ CASES = [
     ("workspace misaligned", dict(workspace=0x180004), "gfx950", INVALID),
     ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
     ("page 32", dict(page_size=32), "gfx950", UNSUPPORTED),
-    ("gqa 4", dict(num_q_heads=4, workspace_size=pfkv.workspace_bytes(16, 64, 4)), "gfx950", UNSUPPORTED),
-    ("gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32)), "gfx950", UNSUPPORTED),
+    ("gqa 4", dict(num_q_heads=4, workspace_size=pfkv.workspace_bytes(16, 64, 4)), "gfx950", OK),
+    ("gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32)), "gfx950", OK),
+    ("gqa 2", dict(num_q_heads=2, workspace_size=pfkv.workspace_bytes(16, 64, 2)), "gfx950", UNSUPPORTED),
+    ("gqa 64", dict(num_q_heads=64, workspace_size=pfkv.workspace_bytes(16, 64, 64)), "gfx950", UNSUPPORTED),
     ("precision fp8 P", dict(precision=1), "gfx950", OK),
     ("precision fp8 Q/P", dict(precision=2), "gfx950", OK),
     ("precision 3", dict(precision=3), "gfx950", INVALID),
