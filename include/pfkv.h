@@ -9,7 +9,8 @@
  * query tokens (1..4) and KV length L_b, every query head attends with a softmax
  * to the first L_b positions of the paged fp8 KV cache, query i (0-based) seeing
  * positions 0 .. L_b - n_b + i (a causal mask over the last n_b positions). The
- * cache is NHD with 16-token pages and head_dim 256; K and V are e4m3fn bytes
+ * cache is NHD with 16-token pages (also 32 or 64 here: a page of 16 R tokens is
+ * R 16-token blocks back to back) and head_dim 256; K and V are e4m3fn bytes
  * whose real values are byte * k_descale (resp. v_descale); G = Hq / Hkv query
  * heads share each KV head, query head hq reading KV head hq / G. The pages'
  * kernel serves G = 16 and 8 (aiter PR #5190, Supported); this library also
@@ -67,7 +68,7 @@ typedef struct pfkv_args {
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
   int32_t head_dim;            /* must be 256 */
-  int32_t page_size;           /* must be 16 */
+  int32_t page_size;           /* 16 (the pages' kernel), 32 or 64 */
   int32_t num_pages;           /* pages in k_cache / v_cache */
   int32_t max_pages_per_seq;   /* columns of block_tables that may be read */
   int32_t num_segments;        /* S in [1, 64] */

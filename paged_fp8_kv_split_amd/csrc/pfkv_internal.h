@@ -39,6 +39,9 @@ struct MainParams {
   // 2 when 32 query heads share a KV head: each KV head is served by two
   // work-groups of 16 query heads (blockIdx.z = 2 kv_head + half), else 1
   int32_t kv_split;
+  // cache pages of 16 << page_ratio_log2 tokens; num_pages counts cache pages,
+  // max_pages_per_seq counts 16-token blocks
+  int32_t page_ratio_log2;
   int32_t precision;           // 0: 16-bit Q/P, 1: e4m3 P, 2: e4m3 Q (per-row scale) and P
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device

@@ -192,6 +192,7 @@ struct PageStream {
   unsigned ids_lds;           // this wave's two page-id windows
   const int* ids;
   int pb, pe, slot, n_steps, num_pages;
+  int rlog;                   // log2(cache page size / 16)
   int next_id;                // block-table entry of the next transfer (read from LDS)
 
   // In LDS, the 16-byte chunk at position pos of key row k (page slot j) holds
@@ -207,6 +208,7 @@ struct PageStream {
     pe = geo.pe;
     n_steps = geo.n_steps;
     num_pages = p.num_pages;
+    rlog = p.page_ratio_log2;
     const int g = lane >> 4, n = lane & 15, jpar = slot & 1;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -220,18 +222,27 @@ struct PageStream {
   }
   __device__ bool has(int t) const { return t < n_steps && pb + kPagesPerStep * t + slot < pe; }
   __device__ int count(int t) const { return has(t) ? kDmaPerWave : 0; }
-  // entry k of window w (w even / odd in two slots) is the page of step 64 w + k
+  // Pages here are 16-token blocks. A cache page of 16 R tokens (R = 2^rlog)
+  // holds R of them back to back in NHD order, so 16-token block pidx is part
+  // pidx mod R of cache page block_tables[pidx / R], at 16-token index
+  // block_tables[pidx / R] R + pidx mod R.
+  // Entry k of window w (w even / odd in two slots) is the table entry of step 64 w + k.
   __device__ void fetch_window(int win, int lane) {
     int pidx = pb + kPagesPerStep * (64 * win + lane) + slot;
     pidx = pidx < pe ? pidx : pb;                      // lanes past the segment read a valid entry
-    dma_4b(bt_row, (unsigned)(4 * pidx), ids_lds + (win & 1) * 256);
+    dma_4b(bt_row, (unsigned)(4 * (pidx >> rlog)), ids_lds + (win & 1) * 256);
+  }
+  // 16-token block of step t from its table entry (clamped into the cache first)
+  __device__ int resolve(int t, int entry) const {
+    const int id = min(max(entry, 0), num_pages - 1);
+    return (id << rlog) + ((pb + kPagesPerStep * t + slot) & ((1 << rlog) - 1));
   }
   __device__ int read_id(int t) const { return ids[((t >> 6) & 1) * 64 + (t & 63)]; }
   __device__ int first_id(int t) const {            // scalar load, before the windows land
-    return ((const const_i32*)bt_row)[has(t) ? pb + kPagesPerStep * t + slot : pb];
+    return ((const const_i32*)bt_row)[(has(t) ? pb + kPagesPerStep * t + slot : pb) >> rlog];
   }
-  __device__ void put(int t, int id) {
-    id = min(max(id, 0), num_pages - 1);
+  __device__ void put(int t, int entry) {
+    const int id = resolve(t, entry);
     const uint8_t* base = cache + (uint64_t)id * page_stride;
     const unsigned dst = ring + (t % kStages) * kStageBytes;
 #pragma unroll
@@ -257,7 +268,7 @@ struct PageStream {
     Pending q{nullptr, 0u, has(t)};
     if (q.on) {
       if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
-      const int id = min(max(__builtin_amdgcn_readfirstlane(next_id), 0), num_pages - 1);
+      const int id = resolve(t, __builtin_amdgcn_readfirstlane(next_id));
       q.base = cache + (uint64_t)id * page_stride;
       q.dst = ring + (t % kStages) * kStageBytes;
       next_id = read_id(t + 1);

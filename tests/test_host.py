@@ -100,7 +100,12 @@ CASES = [
     ("out stride", dict(out_stride_head=2), "gfx950", INVALID),
     ("workspace misaligned", dict(workspace=0x180004), "gfx950", INVALID),
     ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
-    ("page 32", dict(page_size=32), "gfx950", UNSUPPORTED),
+    ("page 32", dict(page_size=32), "gfx950", OK),
+    ("page 64", dict(page_size=64), "gfx950", OK),
+    ("page 8", dict(page_size=8), "gfx950", UNSUPPORTED),
+    ("page 128", dict(page_size=128), "gfx950", UNSUPPORTED),
+    ("page 64 table too wide", dict(page_size=64, max_pages_per_seq=(1 << 25), block_table_stride=(1 << 25)),
+     "gfx950", INVALID),
     ("gqa 4", dict(num_q_heads=4, workspace_size=pfkv.workspace_bytes(16, 64, 4)), "gfx950", OK),
     ("gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32)), "gfx950", OK),
     ("gqa 2", dict(num_q_heads=2, workspace_size=pfkv.workspace_bytes(16, 64, 2)), "gfx950", UNSUPPORTED),
