@@ -29,6 +29,7 @@ from .attention import (  # noqa: F401
     attend_lse,
     bf16_bits_to_f64,
     e4m3fn_decode_table,
+    first_visible_key,
     segment_page_ranges,
     segment_partials,
     visible_key_count,

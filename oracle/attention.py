@@ -27,6 +27,8 @@ problem, with no blocking, fusion or reordering beyond it:
 6. Softmax over the visible keys with exact ``exp`` in fp64, then the weighted
    sum of V rows. A query with no visible key yields zeros.
 7. The optional log-sum-exp of the same scores (:func:`attend_lse`).
+8. Options the pages only name (a left window, a score soft-cap, per-head sink
+   logits), in their common reading (:func:`attend`).
 """
 
 from __future__ import annotations
@@ -92,8 +94,28 @@ def _gather_sequence(table, cache, block_row, seq_len, descale):
     return table[codes] * descale
 
 
+def first_visible_key(seq_len: int, q_len: int, i: int, window_left: int) -> int:
+    """First KV position query i may attend to under a left window.
+
+    The window convention of the varlen attention APIs that aiter PR #7375
+    routes through (section Changes: a negative window is unlimited): query i at
+    position seq_len - q_len + i sees positions from that position minus
+    ``window_left`` on (never before 0).
+    """
+    if window_left < 0:
+        return 0
+    return max(0, seq_len - q_len + i - window_left)
+
+
+def _softcapped(scores: np.ndarray, softcap: float) -> np.ndarray:
+    """cap * tanh(score / cap) when cap > 0 (a score soft-cap), else the scores."""
+    if softcap > 0.0:
+        return softcap * np.tanh(scores / softcap)
+    return scores
+
+
 def attend(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
-           k_descale, v_descale, softmax_scale) -> np.ndarray:
+           k_descale, v_descale, softmax_scale, window_left=-1, softcap=0.0, sinks=None) -> np.ndarray:
     """Exact masked softmax attention; returns float64 ``[T, Hq, D]``.
 
     q: bf16 bit patterns (uint16) or real values, ``[T, Hq, D]`` packed by
@@ -101,6 +123,15 @@ def attend(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
     ``[num_pages, page_size, Hkv, D]``. block_tables: int ``[N, max_pages]``.
     seq_lens: int ``[N]``. cu_seqlens_q: int ``[N + 1]``. The descales and the
     softmax scale are taken at float32 precision, as the device receives them.
+
+    Options the pages name only as features their gates exclude (SGLang PR
+    #37465, Modifications: no sliding window, soft-cap or sinks; aiter PR #7375,
+    Changes: windows, sinks, soft-cap), taken in their common reading:
+    ``window_left`` >= 0 keeps only the keys at most that many positions before
+    the query (:func:`first_visible_key`); ``softcap`` > 0 replaces every score
+    s by softcap * tanh(s / softcap); ``sinks`` (float ``[Hq]``) adds exp(sink)
+    of the row's head to the softmax denominator, a probability mass that
+    carries no value.
     """
     table = e4m3fn_decode_table()
     qf = _queries_f64(q)
@@ -112,10 +143,12 @@ def attend(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
     kd = float(np.float32(k_descale))
     vd = float(np.float32(v_descale))
     scale = float(np.float32(softmax_scale))
+    cap = float(np.float32(softcap))
 
     total_q, num_q_heads, head_dim = qf.shape
     num_kv_heads = k_cache.shape[2]
     group = num_q_heads // num_kv_heads
+    sink = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
     out = np.zeros((total_q, num_q_heads, head_dim), dtype=np.float64)
 
     for b in range(len(seq_lens)):
@@ -128,18 +161,22 @@ def attend(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
         for h in range(num_kv_heads):
             heads = slice(h * group, (h + 1) * group)
             for i in range(q_len):
+                lo = first_visible_key(seq_len, q_len, i, window_left)
                 vis = visible_key_count(seq_len, q_len, i)
-                if vis == 0:
+                if vis <= lo:
                     continue
-                scores = (qf[q0 + i, heads, :] @ keys[:vis, h, :].T) * scale  # [G, vis]
+                scores = _softcapped((qf[q0 + i, heads, :] @ keys[lo:vis, h, :].T) * scale, cap)   # [G, n]
                 top = scores.max(axis=1, keepdims=True)
                 weights = np.exp(scores - top)
-                out[q0 + i, heads, :] = (weights @ vals[:vis, h, :]) / weights.sum(axis=1, keepdims=True)
+                den = weights.sum(axis=1, keepdims=True)
+                if sink is not None:
+                    den = den + np.exp(sink[heads][:, None] - top)
+                out[q0 + i, heads, :] = (weights @ vals[lo:vis, h, :]) / den
     return out
 
 
 def attend_lse(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
-               k_descale, v_descale, softmax_scale) -> np.ndarray:
+               k_descale, v_descale, softmax_scale, window_left=-1, softcap=0.0, sinks=None) -> np.ndarray:
     """Exact log-sum-exp of each row's visible scores; returns float64 ``[T, Hq]``.
 
     lse[t, h] = ln sum_j exp(score_j) over the keys row (t, h) may see, with the
@@ -148,6 +185,8 @@ def attend_lse(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
     -inf for rows that have no finite value). Evaluated as top + ln sum_j
     exp(score_j - top) so that no exp overflows. ``v_cache`` and ``v_descale``
     do not enter; they are accepted so that the call matches :func:`attend`.
+    The options are those of :func:`attend`; a sink adds exp(sink) to the sum,
+    so a row with a sink and no visible key gets lse = sink.
     """
     table = e4m3fn_decode_table()
     qf = _queries_f64(q)
@@ -156,10 +195,12 @@ def attend_lse(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
     cu = np.asarray(cu_seqlens_q)
     kd = float(np.float32(k_descale))
     scale = float(np.float32(softmax_scale))
+    cap = float(np.float32(softcap))
 
     total_q, num_q_heads, _ = qf.shape
     num_kv_heads = k_cache.shape[2]
     group = num_q_heads // num_kv_heads
+    sink = None if sinks is None else np.asarray(sinks, dtype=np.float32).astype(np.float64)
     lse = np.full((total_q, num_q_heads), -np.inf)
 
     for b in range(len(seq_lens)):
@@ -171,10 +212,15 @@ def attend_lse(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
         for h in range(num_kv_heads):
             heads = slice(h * group, (h + 1) * group)
             for i in range(q_len):
+                lo = first_visible_key(seq_len, q_len, i, window_left)
                 vis = visible_key_count(seq_len, q_len, i)
-                if vis == 0:
+                if vis <= lo:
+                    if sink is not None:
+                        lse[q0 + i, heads] = sink[heads]
                     continue
-                scores = (qf[q0 + i, heads, :] @ keys[:vis, h, :].T) * scale  # [G, vis]
+                scores = _softcapped((qf[q0 + i, heads, :] @ keys[lo:vis, h, :].T) * scale, cap)
+                if sink is not None:
+                    scores = np.concatenate([scores, sink[heads][:, None]], axis=1)
                 top = scores.max(axis=1)
                 lse[q0 + i, heads] = top + np.log(np.exp(scores - top[:, None]).sum(axis=1))
     return lse

@@ -129,6 +129,97 @@ def _brute_force_lse(case):
     return lse
 
 
+def _brute_force_options(case, window_left, softcap, sinks):
+    """(out, lse) with a left window, a score soft-cap and sink logits, in pure Python."""
+    a = case.host_arrays()
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()
+    q = case.q.to(torch.float64).numpy()
+    kc, vc, bt = a["k_cache"], a["v_cache"], a["block_tables"]
+    page, hkv, d = kc.shape[1], kc.shape[2], kc.shape[3]
+    hq = q.shape[1]
+    kd, vd, sc = (float(np.float32(a[k])) for k in ("k_descale", "v_descale", "softmax_scale"))
+    out = np.zeros(q.shape)
+    lse = np.full(q.shape[:2], -math.inf)
+    cu = a["cu_seqlens_q"]
+    for b, seq_len in enumerate(a["seq_lens"]):
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t = int(cu[b]) + i
+            pos = int(seq_len) - n + i
+            for head in range(hq):
+                kvh = head // (hq // hkv)
+                scores, rows = [], []
+                for j in range(int(seq_len)):
+                    if j > pos or (window_left >= 0 and j < pos - window_left):
+                        continue
+                    pg, slot = int(bt[b][j // page]), j % page
+                    x = math.fsum(q[t, head, e] * dec[kc[pg, slot, kvh, e]] * kd for e in range(d)) * sc
+                    scores.append(softcap * math.tanh(x / softcap) if softcap > 0 else x)
+                    rows.append([dec[vc[pg, slot, kvh, e]] * vd for e in range(d)])
+                terms = scores + ([float(np.float32(sinks[head]))] if sinks is not None else [])
+                if not terms:
+                    continue
+                top = max(terms)
+                w = [math.exp(x - top) for x in scores]
+                den = math.fsum(math.exp(x - top) for x in terms)
+                lse[t, head] = top + math.log(den)
+                for e in range(d):
+                    out[t, head, e] = math.fsum(w[j] * rows[j][e] for j in range(len(w))) / den
+    return out, lse
+
+
+OPTION_CASES = [
+    dict(window_left=5, softcap=0.0, sinks=None),
+    dict(window_left=0, softcap=0.0, sinks=None),
+    dict(window_left=-1, softcap=2.0, sinks=None),
+    dict(window_left=-1, softcap=0.0, sinks=[0.5, -1.0, 3.0, -20.0]),
+    dict(window_left=17, softcap=1.5, sinks=[1.0, 2.0, -0.5, 0.0]),
+]
+
+
+@pytest.mark.parametrize("opts", OPTION_CASES, ids=[str(i) for i in range(len(OPTION_CASES))])
+def test_oracle_options_match_brute_force(opts):
+    case = _tiny([40, 9, 23], [4, 2, 3], 4, 1, d=8, page=4, seed=31, descale="fixed")
+    arrs = case.host_arrays()
+    got = oracle.attend(**arrs, **opts)
+    got_lse = oracle.attend_lse(**arrs, **opts)
+    ref, ref_lse = _brute_force_options(case, **opts)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * max(np.abs(ref).max(), 1e-300))
+    assert np.array_equal(np.isinf(got_lse), np.isinf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert np.allclose(got_lse[fin], ref_lse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_oracle_option_closed_forms():
+    d = 8
+    k_codes = np.stack([np.full((1, d), c, np.uint8) for c in (0x30, 0x38, 0x40, 0x44, 0x48)])   # 0.5, 1, 2, 3, 4
+    v_codes = np.stack([np.full((1, d), c, np.uint8) for c in (0x38, 0x40, 0x44, 0x48, 0x4c)])   # 1, 2, 3, 4, 6
+    q_vals = np.full((4, 1, d), 0.25)
+    prob = _single_page_problem(k_codes, v_codes, q_vals, q_len=4, scale=0.5)
+    score = [0.5 * 0.25 * d * k for k in (0.5, 1.0, 2.0, 3.0, 4.0)]
+    # window 0: each query sees only its own position
+    out0 = oracle.attend(**prob, window_left=0)
+    lse0 = oracle.attend_lse(**prob, window_left=0)
+    for i in range(4):
+        pos = 1 + i
+        assert np.all(out0[i, 0] == (1.0, 2.0, 3.0, 4.0, 6.0)[pos])
+        assert lse0[i, 0] == pytest.approx(score[pos], rel=1e-15)
+    # a window at least the sequence length is no window
+    assert np.array_equal(oracle.attend(**prob, window_left=5), oracle.attend(**prob))
+    # soft-cap on a single visible key: lse = cap tanh(s / cap), out unchanged
+    one = _single_page_problem(k_codes[:1], v_codes[:1], q_vals[:1], q_len=1, scale=0.5)
+    assert oracle.attend_lse(**one, softcap=0.375)[0, 0] == pytest.approx(0.375 * math.tanh(score[0] / 0.375),
+                                                                         rel=1e-14)
+    assert np.all(oracle.attend(**one, softcap=0.375) == 1.0)
+    # a sink on a single key: out = v sigmoid(s - sink), lse = logaddexp(s, sink)
+    sink = 0.75
+    out_s = oracle.attend(**one, sinks=[sink])
+    assert out_s[0, 0, 0] == pytest.approx(1.0 / (1.0 + math.exp(sink - score[0])), rel=1e-14)
+    assert oracle.attend_lse(**one, sinks=[sink])[0, 0] == pytest.approx(np.logaddexp(score[0], sink), rel=1e-14)
+    # a sink of -inf is no sink
+    assert np.array_equal(oracle.attend(**prob, sinks=[-np.inf]), oracle.attend(**prob))
+
+
 BRUTE_CASES = [
     dict(ctx=[13], q_lens=[4], hq=2, hkv=1),
     dict(ctx=[1, 7, 40], q_lens=[1, 3, 4], hq=4, hkv=2),
@@ -405,6 +496,28 @@ def test_planted_mistake_is_caught_in_lse(monkeypatch, name):
     got = oracle_attention.attend_lse(**case.host_arrays())
     fin = np.isfinite(ref) & np.isfinite(got)
     assert not (np.array_equal(np.isinf(got), np.isinf(ref)) and np.allclose(got[fin], ref[fin], rtol=1e-6, atol=1e-9))
+
+
+def _option_mutations():
+    good_first = oracle_attention.first_visible_key
+    good_cap = oracle_attention._softcapped
+    return {
+        "window_off_by_one": ("first_visible_key", lambda L, n, i, w: good_first(L, n, i, w) + (1 if w >= 0 else 0)),
+        "window_ignored": ("first_visible_key", lambda L, n, i, w: 0),
+        "softcap_outer_factor_dropped": ("_softcapped", lambda x, c: np.tanh(x / c) if c > 0 else x),
+        "softcap_ignored": ("_softcapped", lambda x, c: x),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_option_mutations()))
+def test_planted_option_mistake_is_caught(monkeypatch, name):
+    attr, bad = _option_mutations()[name]
+    case = _tiny([40, 9, 23], [4, 2, 3], 4, 1, d=8, page=4, seed=31, descale="fixed")
+    opts = dict(window_left=6, softcap=1.5, sinks=None)
+    ref, _ = _brute_force_options(case, **opts)
+    monkeypatch.setattr(oracle_attention, attr, bad)
+    got = oracle_attention.attend(**case.host_arrays(), **opts)
+    assert not np.allclose(got, ref, rtol=1e-6, atol=1e-9)
 
 
 @pytest.mark.parametrize("name", sorted(_mutations()))
