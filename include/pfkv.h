@@ -76,7 +76,26 @@ typedef struct pfkv_args {
   int32_t precision;           /* PFKV_PRECISION_* below */
   float* lse;                  /* optional, NULL = not written: fp32 [num_q_heads, total_q], element (h, t)
                                   at lse[h * total_q + t], 4-B aligned; see below */
+  const float* sinks;          /* optional, NULL = none: fp32 [num_q_heads] sink logits, 4-B aligned */
+  int32_t window_keys;         /* > 0: a query sees only its window_keys most recent keys (itself included);
+                                  <= 0 (the zero-initialised default): all */
+  float softcap;               /* > 0: every score s becomes softcap * tanh(s / softcap); 0: off */
 } pfkv_args;
+
+/*
+ * Options that the pages name only as features their gates leave out (SGLang
+ * PR #37465, Modifications: no sliding window, soft-cap or sinks; aiter PR
+ * #7375, Changes: windows, sinks, soft-cap), in their common reading. With a
+ * score s_j = softmax_scale * <q, k_j> (K descaled):
+ *  - window_keys = W + 1 > 0: query i of a sequence (position L - n + i) sees
+ *    keys L - n + i - W .. L - n + i, i.e. a left window of W positions (the
+ *    convention that aiter PR #7375, Changes, applies, where a negative left
+ *    window is unlimited; here 0 keeps zero-initialised arguments unlimited).
+ *    The segments then partition only the pages some query can see.
+ *  - softcap c > 0: s_j -> c tanh(s_j / c) before the softmax.
+ *  - sinks: out = sum_j e^(s_j) v_j / (sum_j e^(s_j) + e^(sink_h)) and the sink
+ *    adds e^(sink_h) to the lse sum: a probability mass that carries no value.
+ */
 
 /*
  * Log-sum-exp output (aiter PR #7375, Summary and Behavior and intent: an

@@ -66,6 +66,9 @@ class PfkvArgs(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("precision", ctypes.c_int32),
         ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+        ("window_keys", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -153,10 +156,12 @@ PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
 
 
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-               softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None) -> PfkvArgs:
+               softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None,
+               sinks=None, window_left=-1, softcap=0.0) -> PfkvArgs:
     """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here).
 
-    ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device.
+    ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device,
+    ``sinks`` (optional) a contiguous float32 ``[Hq]`` tensor on q's device.
     """
     k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
@@ -213,17 +218,29 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.softmax_scale = float(softmax_scale)
     a.precision = int(precision)
     a.lse = lse.data_ptr() if lse is not None else None
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or tuple(sinks.shape) != (q.shape[1],) or not sinks.is_contiguous():
+            raise TypeError("sinks must be a contiguous float32 [Hq] tensor")
+        if sinks.device != q.device:
+            raise ValueError(f"sinks must be on q's device ({q.device}), got {sinks.device}")
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.window_keys = int(window_left) + 1 if window_left >= 0 else 0   # left window W -> W + 1 keys
+    a.softcap = float(softcap)
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                 softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
-                precision=PRECISION_16BIT, return_lse=False, lse=None):
+                precision=PRECISION_16BIT, return_lse=False, lse=None, sinks=None, window_left=-1,
+                softcap=0.0):
     """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``), or
     ``(out, lse)`` when ``return_lse`` is set or an ``lse`` buffer is given.
 
     ``lse`` is float32 ``[Hq, T]``: the natural-log sum of exp(scores) over each
     row's visible keys, -inf for a row without one (``include/pfkv.h``).
+    ``sinks`` (float32 ``[Hq]``), ``window_left`` (a left window of that many
+    positions when >= 0; passed as ``window_keys = window_left + 1``) and
+    ``softcap`` (> 0 to enable) are the options described in ``include/pfkv.h``.
     ``num_segments=None`` picks the library heuristic from the device's CU count.
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
@@ -245,7 +262,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     if return_lse and lse is None:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-                   softmax_scale, num_segments, out, workspace, precision, lse)
+                   softmax_scale, num_segments, out, workspace, precision, lse, sinks, window_left, softcap)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -131,6 +131,8 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
     return fail(PFKV_INVALID, "precision must be one of PFKV_PRECISION_16BIT, _FP8_P, _FP8");
   if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
     return fail(PFKV_INVALID, "softmax_scale must be finite and positive");
+  if (!std::isfinite(a->softcap) || a->softcap < 0.f)
+    return fail(PFKV_INVALID, "softcap must be finite and >= 0 (0 = off)");
   if (a->q_stride_token <= 0 || a->q_stride_head <= 0 || a->out_stride_token <= 0 || a->out_stride_head <= 0)
     return fail(PFKV_INVALID, "q / out strides must be positive");
   if (a->q_stride_token % 8 || a->q_stride_head % 8 || !aligned(a->q, 16))
@@ -148,7 +150,7 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (!aligned(a->k_cache, 16) || !aligned(a->v_cache, 16))
     return fail(PFKV_INVALID, "k_cache / v_cache must be 16-byte aligned");
   if (!aligned(a->block_tables, 4) || !aligned(a->seq_lens, 4) || !aligned(a->cu_seqlens_q, 4) ||
-      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4) || !aligned(a->lse, 4))
+      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4) || !aligned(a->lse, 4) || !aligned(a->sinks, 4))
     return fail(PFKV_INVALID, "int32 / fp32 arguments must be 4-byte aligned");
   const uint64_t need = pfkv_workspace_bytes(a->num_segments, a->total_q, a->num_q_heads);
   if (a->workspace_size < need)
@@ -213,6 +215,10 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
     st = check_device_pointer(a->lse, device, "lse");
     if (st != PFKV_OK) return st;
   }
+  if (a->sinks != nullptr) {
+    st = check_device_pointer(a->sinks, device, "sinks");
+    if (st != PFKV_OK) return st;
+  }
 
   const int group = a->num_q_heads / a->num_kv_heads;
   const uint64_t part_rows = (uint64_t)a->num_segments * a->total_q * a->num_q_heads;
@@ -239,6 +245,9 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.out_stride_head = a->out_stride_head;
   m.v_descale = a->v_descale;
   m.lse = a->lse;
+  m.sinks = a->sinks;
+  m.window_left = a->window_keys > 0 ? a->window_keys - 1 : -1;
+  m.softcap = a->softcap;
   m.direct = a->num_segments == 1 ? 1 : 0;
   m.kv_split = group == 32 ? 2 : 1;
   m.precision = a->precision;
@@ -259,6 +268,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   rp->out_stride_token = a->out_stride_token;
   rp->out_stride_head = a->out_stride_head;
   rp->lse = a->lse;
+  rp->sinks = a->sinks;
   rp->total_q = a->total_q;
   rp->num_q_heads = a->num_q_heads;
   rp->num_segments = a->num_segments;

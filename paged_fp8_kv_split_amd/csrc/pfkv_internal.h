@@ -35,6 +35,9 @@ struct MainParams {
   int64_t out_stride_token, out_stride_head;
   const float* v_descale;
   float* lse;                  // optional [Hq][T] fp32, written here when direct
+  const float* sinks;          // optional [Hq] fp32 sink logits (used here when direct)
+  int32_t window_left;         // < 0: no window
+  float softcap;               // > 0: scores soft-capped
   int32_t direct;              // num_segments == 1
   // 2 when 32 query heads share a KV head: each KV head is served by two
   // work-groups of 16 query heads (blockIdx.z = 2 kv_head + half), else 1
@@ -54,6 +57,7 @@ struct ReduceParams {
   uint16_t* out;               // bf16 bits
   int64_t out_stride_token, out_stride_head;
   float* lse;                  // optional [Hq][T] fp32
+  const float* sinks;          // optional [Hq] fp32 sink logits
   int32_t total_q, num_q_heads, num_segments;
 };
 

@@ -10,7 +10,9 @@
 // s = 0, 1, ...; the denominator by a fixed butterfly over the wave's lanes.
 // With an lse buffer the row's log-sum-exp ln 2 (M + log2 sum_s c_s) goes to
 // lse[hq][t] (-inf when the sum is 0), the merge rule of split softmax
-// statistics (aiter PR #7375, Behavior and intent).
+// statistics (aiter PR #7375, Behavior and intent). A sink logit of the row's
+// head adds e^sink to the denominator (and to the lse sum) and nothing to the
+// numerator.
 // One wave per output row: lane s holds (m_s, l_s), every lane four dims of
 // the fp16 o rows, whose loads for up to 16 segments are in flight together.
 #include "pfkv_internal.h"
@@ -70,15 +72,24 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
     for (int k = 0; k < kBatch; ++k)
       if (s0 + k < S) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
   }
-  const float vd = *(const const_f32*)p.v_descale;
-  const float inv = den > 0.f ? vd / den : 0.f;
   const int64_t t = row / p.num_q_heads, hq = row - t * p.num_q_heads;
+  // a sink logit (log2 units here) joins the denominator: with Mx = max(M, sink),
+  // out = num 2^(M - Mx) / (den 2^(M - Mx) + 2^(sink - Mx))
+  float scale = 1.f, Mx = M;
+  if (p.sinks != nullptr) {
+    const float sink2 = ((const const_f32*)p.sinks)[hq] * 1.44269504088896341f;
+    Mx = fmaxf(M, sink2);
+    scale = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mx);
+    den = den * scale + __builtin_amdgcn_exp2f(sink2 - Mx);
+  }
+  const float vd = *(const const_f32*)p.v_descale;
+  const float inv = den > 0.f ? vd * scale / den : 0.f;
   uint16_t* dst = p.out + t * p.out_stride_token + hq * p.out_stride_head + 4 * lane;
   const uint32_t lo = bf16_rne(num[0] * inv) | (bf16_rne(num[1] * inv) << 16);
   const uint32_t hi = bf16_rne(num[2] * inv) | (bf16_rne(num[3] * inv) << 16);
   *(uint2*)dst = make_uint2(lo, hi);
   if (p.lse != nullptr && lane == 0)
-    p.lse[hq * p.total_q + t] = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
+    p.lse[hq * p.total_q + t] = den > 0.f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 }  // namespace

@@ -95,7 +95,7 @@ struct Cfg {
   static constexpr int kLdsBytes = kOffStage + 2 * kStages * kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][256]
-  static_assert(kPagesPerStep * kRows * 4 <= kOffObuf, "epilogue row sums");
+  static_assert((kPagesPerStep + 1) * kRows * 4 <= kOffObuf, "epilogue row sums and sink terms");
   static_assert(kOffObuf + kRows * kHeadDim * 2 <= kLdsBytes, "epilogue o staging");
 };
 
@@ -178,6 +178,7 @@ struct Geo {
   int seg, b, h;     // h: this work-group's group of G query heads (query heads h G .. h G + G - 1)
   int hkv;           // the KV head those query heads read
   int q0, q_len, L, pb, pe, rows, n_steps;
+  int win;           // left window (clamped to L), -1 when none
   float c2;          // k_descale * softmax_scale * log2(e): raw score -> log2 units
 };
 
@@ -330,6 +331,11 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   const int h = geo.h, q0 = geo.q0, q_len = geo.q_len, L = geo.L, pb = geo.pb;
   const int rows = geo.rows, n_steps = geo.n_steps;
   const float c2 = geo.c2;
+  // left window: the first step of a segment that starts below the largest
+  // lower key bound (that of the last query row) masks keys from below
+  const int win = geo.win;
+  const bool win_head = win >= 0 && kPageSize * pb < L - 1 - win;
+  const bool capped = p.softcap > 0.f;
   uint8_t* const k_ring = smem + C::kOffStage;
 
   PageStream ks;   // K of page slot w: streamed by P.V wave w + 4, read here
@@ -361,6 +367,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   bf16x8 qop[F8 ? 1 : NRB][4][2];
   i32x8 q8[F8 ? NRB : 1][2];
   float c2r[NRB], inv_c2r[NRB];
+  float cap_a[NRB], cap_b[NRB];   // soft-cap in raw-score units: s -> cap_b tanh(cap_a s)
   auto load_q = [&]() {
     if constexpr (F8) {
 #pragma unroll
@@ -473,15 +480,27 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
           }
         }
       }
-      if (kTail && kPageSize * (pidx + 1) > L - q_len + 1) {
+      if (capped) {
+        // s -> cap tanh(s / cap) in the row's raw-score units; tanh y =
+        // 1 - 2 / (1 + e^(2y)), which saturates to +-1 without overflow
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(2.88539008177792681f * cap_a[rb] * sv[rb][r]);
+            sv[rb][r] = cap_b[rb] * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
+          }
+      }
+      if (kTail && (kPageSize * (pidx + 1) > L - q_len + 1 || (win >= 0 && kPageSize * pidx < L - 1 - win))) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const int i = (16 * rb + n) / G;
           const int lim = min(L - 1, L - q_len + i);
+          const int lo = win < 0 ? 0 : L - q_len + i - win;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kPageSize * pidx + 4 * g + r;
-            sv[rb][r] = key <= lim ? sv[rb][r] : -__builtin_inff();
+            sv[rb][r] = (key <= lim && key >= lo) ? sv[rb][r] : -__builtin_inff();
           }
         }
       }
@@ -572,7 +591,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
     if (have_p) form_p(t - 1, (kst + 3) & 1, flag_word);
     if (have_s) {
-      if (kTail && t + 2 >= n_steps)
+      if (kTail && (t + 2 >= n_steps || (t == 0 && win_head)))
         score_step(t, kraw, std::true_type{});
       else
         score_step(t, kraw, std::false_type{});
@@ -590,6 +609,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   if (n_steps > 0) {
     lds_barrier();   // Q and step 0's K are in LDS
     load_q();
+    if (capped) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        cap_a[rb] = c2r[rb] * 0.69314718055994531f / p.softcap;
+        cap_b[rb] = 1.f / cap_a[rb];
+      }
+    }
     int t = 0;
     for (; t < 4 && t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
     for (; t + 7 < n_steps; t += 4) {
@@ -613,6 +639,14 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (g == 0) lsum[w * C::kRows + 16 * rb + n] = l;
+    // one segment with sink logits: the sink's share of the denominator,
+    // 2^(sink - m), joins the row sums as a fifth slot for the P.V waves
+    if (g == 0 && w == 0 && p.direct && p.sinks != nullptr) {
+      const int row = 16 * rb + n;
+      const int gg = (row < rows ? row : 0) % G;
+      const float sink2 = ((const const_f32*)p.sinks)[h * G + gg] * 1.44269504088896341f;
+      lsum[kPagesPerStep * C::kRows + row] = __builtin_amdgcn_exp2f(sink2 - m_ref[rb]);
+    }
   }
   lds_barrier();   // row sums of every page slot
   if (w == 0 && g == 0 && (!p.direct || p.lse != nullptr)) {
@@ -626,9 +660,17 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
         const int i = row / G, gg = row - (row / G) * G;
         if (p.direct) {
-          // one segment: the row's log-sum-exp goes straight to lse (natural log)
+          // one segment: the row's log-sum-exp goes straight to lse (natural
+          // log), a sink logit joining the sum as 2^(sink - mx), mx = max(m, sink)
+          float mx = m_ref[rb], den = l;
+          if (p.sinks != nullptr) {
+            const float sink2 = ((const const_f32*)p.sinks)[h * G + gg] * 1.44269504088896341f;
+            mx = fmaxf(m_ref[rb], sink2);
+            den = (m_ref[rb] == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(m_ref[rb] - mx)) +
+                  __builtin_amdgcn_exp2f(sink2 - mx);
+          }
           p.lse[(int64_t)(h * G + gg) * T + q0 + i] =
-              l > 0.f ? (m_ref[rb] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -__builtin_inff();
+              den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
         } else {
           float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
           // streaming stores: the partials are read once, by the reduce
@@ -927,6 +969,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           float l = lsum[row];
 #pragma unroll
           for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
+          if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
           const float inv = l > 0.f ? vd / l : 0.f;
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt) {
@@ -948,6 +991,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         float l = lsum[row];
 #pragma unroll
         for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
+        if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
         // o = acc / l (0 with no visible key); a single segment writes out = vd o
         const float inv = l > 0.f ? vd / l : 0.f;
 #pragma unroll
@@ -995,9 +1039,15 @@ splitkv_main_kernel(MainParams p) {
   geo.q_len = q_len;
   geo.L = min(max(sl[geo.b], 0), p.max_pages_per_seq * kPageSize);
   const int pages = (geo.L + kPageSize - 1) / kPageSize;
-  const int chunk = (pages + p.num_segments - 1) / p.num_segments;
-  geo.pb = min(geo.seg * chunk, pages);
-  geo.pe = min(geo.pb + chunk, pages);
+  // with a left window the segments split only the pages some query can see;
+  // the first page is bounded with the largest q_len, so that the partition,
+  // and with it every row's bits, does not depend on the call's q_len
+  geo.win = p.window_left < 0 ? -1 : min(p.window_left, geo.L);
+  const int first = geo.win < 0 ? 0 : min(max(geo.L - kMaxQLen - geo.win, 0) / kPageSize, pages);
+  const int span = pages - first;
+  const int chunk = (span + p.num_segments - 1) / p.num_segments;
+  geo.pb = first + min(geo.seg * chunk, span);
+  geo.pe = first + min(geo.seg * chunk + chunk, span);
   geo.rows = G * q_len;
   geo.n_steps = (geo.pe - geo.pb + kPagesPerStep - 1) / kPagesPerStep;
   geo.c2 = *(const const_f32*)p.k_descale * p.score_scale_log2;

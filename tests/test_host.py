@@ -114,6 +114,13 @@ CASES = [
     ("precision fp8 Q/P", dict(precision=2), "gfx950", OK),
     ("precision 3", dict(precision=3), "gfx950", INVALID),
     ("lse given", dict(lse=0x1c0000), "gfx950", OK),
+    ("sinks given", dict(sinks=0x1d0000), "gfx950", OK),
+    ("sinks misaligned", dict(sinks=0x1d0001), "gfx950", INVALID),
+    ("window one key", dict(window_keys=1), "gfx950", OK),
+    ("window negative", dict(window_keys=-5), "gfx950", OK),
+    ("softcap", dict(softcap=30.0), "gfx950", OK),
+    ("softcap negative", dict(softcap=-1.0), "gfx950", INVALID),
+    ("softcap nan", dict(softcap=float("nan")), "gfx950", INVALID),
     ("lse misaligned", dict(lse=0x1c0002), "gfx950", INVALID),
     ("precision -1", dict(precision=-1), "gfx950", INVALID),
     ("mi300", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
