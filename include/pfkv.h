@@ -64,7 +64,7 @@ typedef struct pfkv_args {
   int64_t block_table_stride;  /* elements between rows of block_tables (>= max_pages_per_seq) */
   uint64_t workspace_size;     /* bytes available at workspace */
   int32_t num_seqs;            /* N >= 1 */
-  int32_t total_q;             /* T = cu_seqlens_q[N], 1 <= T <= 4 N */
+  int32_t total_q;             /* T = cu_seqlens_q[N], 1 <= T <= max_q_len N */
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
   int32_t head_dim;            /* must be 256 */
@@ -80,6 +80,8 @@ typedef struct pfkv_args {
   int32_t window_keys;         /* > 0: a query sees only its window_keys most recent keys (itself included);
                                   <= 0 (the zero-initialised default): all */
   float softcap;               /* > 0: every score s becomes softcap * tanh(s / softcap); 0: off */
+  int32_t max_q_len;           /* bound on every n_b: 0 (the zero-initialised default) = 4, the pages'
+                                  bound; up to 8 (longer drafts); rows of tokens past it are not written */
 } pfkv_args;
 
 /*

@@ -69,6 +69,7 @@ class PfkvArgs(ctypes.Structure):
         ("sinks", ctypes.c_void_p),
         ("window_keys", ctypes.c_int32),
         ("softcap", ctypes.c_float),
+        ("max_q_len", ctypes.c_int32),
     ]
 
 
@@ -157,7 +158,7 @@ PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
 
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None,
-               sinks=None, window_left=-1, softcap=0.0) -> PfkvArgs:
+               sinks=None, window_left=-1, softcap=0.0, max_q_len=0) -> PfkvArgs:
     """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here).
 
     ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device,
@@ -226,13 +227,14 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.window_keys = int(window_left) + 1 if window_left >= 0 else 0   # left window W -> W + 1 keys
     a.softcap = float(softcap)
+    a.max_q_len = int(max_q_len)
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                 softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
                 precision=PRECISION_16BIT, return_lse=False, lse=None, sinks=None, window_left=-1,
-                softcap=0.0):
+                softcap=0.0, max_q_len=0):
     """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``), or
     ``(out, lse)`` when ``return_lse`` is set or an ``lse`` buffer is given.
 
@@ -241,6 +243,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     ``sinks`` (float32 ``[Hq]``), ``window_left`` (a left window of that many
     positions when >= 0; passed as ``window_keys = window_left + 1``) and
     ``softcap`` (> 0 to enable) are the options described in ``include/pfkv.h``.
+    ``max_q_len`` bounds every sequence's query tokens (0 = 4, at most 8).
     ``num_segments=None`` picks the library heuristic from the device's CU count.
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
@@ -262,7 +265,8 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     if return_lse and lse is None:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
-                   softmax_scale, num_segments, out, workspace, precision, lse, sinks, window_left, softcap)
+                   softmax_scale, num_segments, out, workspace, precision, lse, sinks, window_left, softcap,
+                   max_q_len)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -9,6 +9,7 @@
 // q_len 1..4 per sequence as in SGLang PR #37465, Modifications. Unsupported
 // shapes return PFKV_UNSUPPORTED so that a caller can fall back, as the SGLang
 // entry points do.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -114,8 +115,11 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
 
   if (a->num_seqs < 1 || a->num_seqs > (1 << 20)) return fail(PFKV_INVALID, "num_seqs must be in [1, 2^20]");
   if (a->total_q < 1) return fail(PFKV_INVALID, "total_q must be >= 1");
-  if ((int64_t)a->total_q > (int64_t)pfkv::kMaxQLen * a->num_seqs)
-    return fail(PFKV_INVALID, "total_q exceeds 4 query tokens per sequence");
+  if (a->max_q_len < 0 || a->max_q_len > pfkv::kMaxQLen)
+    return fail(PFKV_INVALID, "max_q_len must be in [0, 8] (0 = 4)");
+  const int max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
+  if ((int64_t)a->total_q > (int64_t)max_q_len * a->num_seqs)
+    return fail(PFKV_INVALID, "total_q exceeds max_q_len query tokens per sequence");
   if (a->num_q_heads < 1 || a->num_kv_heads < 1) return fail(PFKV_INVALID, "head counts must be positive");
   if (a->num_kv_heads > 4096) return fail(PFKV_INVALID, "num_kv_heads must be <= 4096");
   if (a->num_q_heads % a->num_kv_heads != 0) return fail(PFKV_INVALID, "num_q_heads % num_kv_heads != 0");
@@ -138,10 +142,11 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (a->q_stride_token % 8 || a->q_stride_head % 8 || !aligned(a->q, 16))
     return fail(PFKV_INVALID, "q rows must be 16-byte aligned (strides multiple of 8 elements)");
   {
-    // the main kernel addresses a (sequence, KV head)'s Q rows with 32-bit byte offsets
+    // the main kernel addresses a work-group's Q rows (its query tokens, at most
+    // max_q_len, times its query heads) with 32-bit byte offsets
     const int64_t group = a->num_q_heads / a->num_kv_heads;
-    const int64_t span = ((int64_t)(pfkv::kMaxQLen - 1) * a->q_stride_token + (group - 1) * a->q_stride_head +
-                          pfkv::kHeadDim) * 2;
+    const int64_t tokens = max_q_len;
+    const int64_t span = ((tokens - 1) * a->q_stride_token + (group - 1) * a->q_stride_head + pfkv::kHeadDim) * 2;
     if (span >= ((int64_t)1 << 32)) return fail(PFKV_INVALID, "q strides too large (a KV head's rows span >= 4 GiB)");
   }
   if (a->out_stride_token % 4 || a->out_stride_head % 4 || !aligned(a->out, 8))
@@ -250,6 +255,14 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.softcap = a->softcap;
   m.direct = a->num_segments == 1 ? 1 : 0;
   m.kv_split = group == 32 ? 2 : 1;
+  {
+    // a work-group stacks at most kMaxRows = 64 query rows: with 16 query heads
+    // per work-group and up to 8 tokens, a sequence's tokens split in two blocks
+    const int g_wg = group == 32 ? 16 : group;
+    const int max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
+    m.q_per_wg = std::min(pfkv::kMaxRows / g_wg, pfkv::kMaxQLen);
+    m.q_split = (max_q_len + m.q_per_wg - 1) / m.q_per_wg;
+  }
   m.precision = a->precision;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;

@@ -8,7 +8,9 @@ namespace pfkv {
 
 constexpr int kHeadDim = 256;   // head_dim served by the kernels
 constexpr int kPageSize = 16;   // tokens per KV page
-constexpr int kMaxQLen = 4;     // query tokens per sequence
+constexpr int kMaxQLen = 8;     // query tokens per sequence (the pages' 4, or up to 8 with max_q_len)
+constexpr int kDefaultMaxQLen = 4;
+constexpr int kMaxRows = 64;    // stacked query rows (G x tokens) per work-group
 constexpr int kMaxSegments = 64;
 
 // Workspace layout, written by the main kernel and read by the reduce:
@@ -42,6 +44,10 @@ struct MainParams {
   // 2 when 32 query heads share a KV head: each KV head is served by two
   // work-groups of 16 query heads (blockIdx.z = 2 kv_head + half), else 1
   int32_t kv_split;
+  // query-token blocks per (sequence, head group): a work-group holds at most
+  // q_per_wg tokens (kMaxRows / G); q_split = 2 when a sequence may have more
+  // (blockIdx.z = head_group * q_split + block)
+  int32_t q_split, q_per_wg;
   // cache pages of 16 << page_ratio_log2 tokens; num_pages counts cache pages,
   // max_pages_per_seq counts 16-token blocks
   int32_t page_ratio_log2;

@@ -83,7 +83,7 @@ template <int G>
 struct Cfg {
   // 16-row MFMA blocks (all rows); at least two, so that the 32-row tiles of
   // the fp8 P.V path stay inside the P, maximum and rescale buffers
-  static constexpr int kRowBlocks = G * kMaxQLen / 16 < 2 ? 2 : G * kMaxQLen / 16;
+  static constexpr int kRowBlocks = G * kMaxQLen / 16 < 2 ? 2 : (G * kMaxQLen / 16 > kMaxRows / 16 ? kMaxRows / 16 : G * kMaxQLen / 16);
   static constexpr int kRows = kRowBlocks * 16;
   static constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;         // fp16 P of a step: [rb][k-step][lane] x 16 B
   static constexpr int kOffP = 0;                                  // two P buffers
@@ -177,7 +177,8 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(unsigned lo, unsigned hi) {
 struct Geo {
   int seg, b, h;     // h: this work-group's group of G query heads (query heads h G .. h G + G - 1)
   int hkv;           // the KV head those query heads read
-  int q0, q_len, L, pb, pe, rows, n_steps;
+  int q0, q_len, L, pb, pe, rows, n_steps;   // q0, q_len: this work-group's query tokens
+  int qoff;          // KV position of the work-group's first query token
   int win;           // left window (clamped to L), -1 when none
   float c2;          // k_descale * softmax_scale * log2(e): raw score -> log2 units
 };
@@ -334,7 +335,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   // left window: the first step of a segment that starts below the largest
   // lower key bound (that of the last query row) masks keys from below
   const int win = geo.win;
-  const bool win_head = win >= 0 && kPageSize * pb < L - 1 - win;
+  const int qoff = geo.qoff;
+  const bool win_head = win >= 0 && kPageSize * pb < qoff + q_len - 1 - win;
   const bool capped = p.softcap > 0.f;
   uint8_t* const k_ring = smem + C::kOffStage;
 
@@ -491,12 +493,12 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
             sv[rb][r] = cap_b[rb] * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
           }
       }
-      if (kTail && (kPageSize * (pidx + 1) > L - q_len + 1 || (win >= 0 && kPageSize * pidx < L - 1 - win))) {
+      if (kTail && (kPageSize * (pidx + 1) > qoff + 1 || (win >= 0 && kPageSize * pidx < qoff + q_len - 1 - win))) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const int i = (16 * rb + n) / G;
-          const int lim = min(L - 1, L - q_len + i);
-          const int lo = win < 0 ? 0 : L - q_len + i - win;
+          const int lim = min(L - 1, qoff + i);
+          const int lo = win < 0 ? 0 : qoff + i - win;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kPageSize * pidx + 4 * g + r;
@@ -1028,16 +1030,21 @@ splitkv_main_kernel(MainParams p) {
   Geo geo;
   geo.seg = blockIdx.x;
   geo.b = blockIdx.y;
-  geo.h = blockIdx.z;
-  geo.hkv = blockIdx.z / p.kv_split;
+  geo.h = blockIdx.z / p.q_split;
+  geo.hkv = geo.h / p.kv_split;
   // out-of-contract values are clamped so that every access stays in its buffer
-  geo.q0 = cu[geo.b];
-  int q_len = cu[geo.b + 1] - geo.q0;
-  if (geo.q0 < 0 || geo.q0 >= p.total_q) q_len = 0;
-  q_len = min(max(q_len, 0), min(kMaxQLen, p.total_q - max(geo.q0, 0)));
+  const int seq_q0 = cu[geo.b];
+  int seq_qlen = cu[geo.b + 1] - seq_q0;
+  if (seq_q0 < 0 || seq_q0 >= p.total_q) seq_qlen = 0;
+  seq_qlen = min(max(seq_qlen, 0), min(kMaxQLen, p.total_q - max(seq_q0, 0)));
+  // this work-group's block of the sequence's query tokens
+  const int i0 = (blockIdx.z % p.q_split) * p.q_per_wg;
+  const int q_len = min(seq_qlen - i0, p.q_per_wg);
   if (q_len <= 0) return;
+  geo.q0 = seq_q0 + i0;
   geo.q_len = q_len;
   geo.L = min(max(sl[geo.b], 0), p.max_pages_per_seq * kPageSize);
+  geo.qoff = geo.L - seq_qlen + i0;
   const int pages = (geo.L + kPageSize - 1) / kPageSize;
   // with a left window the segments split only the pages some query can see;
   // the first page is bounded with the largest q_len, so that the partition,
@@ -1061,12 +1068,17 @@ splitkv_main_kernel(MainParams p) {
       default: verify_segment<16, 4, MODE>(p, geo, smem); break;
     }
   } else if constexpr (G == 8) {
-    if (nrb == 1)
-      verify_segment<8, 1, MODE>(p, geo, smem);
-    else
-      verify_segment<8, 2, MODE>(p, geo, smem);
+    switch (nrb) {
+      case 1: verify_segment<8, 1, MODE>(p, geo, smem); break;
+      case 2: verify_segment<8, 2, MODE>(p, geo, smem); break;
+      case 3: verify_segment<8, 3, MODE>(p, geo, smem); break;
+      default: verify_segment<8, 4, MODE>(p, geo, smem); break;
+    }
   } else {
-    verify_segment<4, 1, MODE>(p, geo, smem);
+    if (nrb == 1)
+      verify_segment<4, 1, MODE>(p, geo, smem);
+    else
+      verify_segment<4, 2, MODE>(p, geo, smem);
   }
 }
 
@@ -1074,7 +1086,7 @@ splitkv_main_kernel(MainParams p) {
 // as two 16-head work-groups, p.kv_split = 2)
 template <int MODE>
 hipError_t launch_mode(const MainParams& p, int group, hipStream_t stream) {
-  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split);
+  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
   if (group == 16)
     hipLaunchKernelGGL((splitkv_main_kernel<16, MODE>), grid, dim3(kThreads), 0, stream, p);
   else if (group == 8)

@@ -84,6 +84,10 @@ CASES = [
     ("null descale", dict(v_descale=0), "gfx950", INVALID),
     ("zero seqs", dict(num_seqs=0), "gfx950", INVALID),
     ("too many queries", dict(total_q=65), "gfx950", INVALID),
+    ("max_q_len 8", dict(max_q_len=8, total_q=128, workspace_size=pfkv.workspace_bytes(16, 128, 16)), "gfx950", OK),
+    ("max_q_len 8 too many queries", dict(max_q_len=8, total_q=129), "gfx950", INVALID),
+    ("max_q_len 9", dict(max_q_len=9), "gfx950", INVALID),
+    ("max_q_len negative", dict(max_q_len=-1), "gfx950", INVALID),
     ("heads not divisible", dict(num_q_heads=15, num_kv_heads=2), "gfx950", INVALID),
     ("zero kv heads", dict(num_kv_heads=0), "gfx950", INVALID),
     ("segments 0", dict(num_segments=0), "gfx950", INVALID),
