@@ -125,7 +125,10 @@ typedef struct pfkv_args {
  *   notes and Accuracy): each query row quantised to e4m3 with scale amax / 448
  *   and both contractions on the fp8 MFMA.
  * With e4m3 P, probabilities below 2^-10 of a row's reference maximum flush to
- * zero (the underflow the aiter PR #7375 review thread works through).
+ * zero (the underflow the aiter PR #7375 review thread works through). With
+ * e4m3 Q, rows that see only a handful of keys can flip close maxima (errors of
+ * 0.5 sigma and more measured with 8 visible keys); the fp8 variants are meant
+ * for long contexts.
  */
 enum pfkv_precision { PFKV_PRECISION_16BIT = 0, PFKV_PRECISION_FP8_P = 1, PFKV_PRECISION_FP8 = 2 };
 
