@@ -157,6 +157,19 @@ int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
 int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);
 
 /*
+ * Debug mode: on (PFKV_DEBUG=1 in the environment at the first call, or
+ * pfkv_set_debug(1)), pfkv_verify_attn_fwd and pfkv_splitkv_main first run a
+ * checking kernel over the device-side preconditions above (cu_seqlens_q
+ * monotone from 0 to total_q, 0 <= n_b <= max_q_len, n_b <= L_b <= page_size *
+ * max_pages_per_seq, used block-table entries in [0, num_pages)) and return
+ * PFKV_INVALID, naming the first offending sequence, without launching the
+ * attention kernels. Debug mode synchronizes the stream and allocates a 16-byte
+ * status buffer per device once: it is not for graph capture. Returns the
+ * previous setting.
+ */
+int pfkv_set_debug(int on);
+
+/*
  * The two stages of pfkv_verify_attn_fwd, exposed separately (same arguments,
  * same validation) so that a caller can place or time them individually:
  * pfkv_splitkv_main enqueues only the split-KV main kernel, which writes the

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     num_segments,
+    set_debug,
     stream_read,
     verify_attn,
     workspace_bytes,

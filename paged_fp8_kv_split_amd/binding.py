@@ -105,8 +105,16 @@ def load_library():
     lib.pfkv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.pfkv_stream_read.restype = ctypes.c_int
+    lib.pfkv_set_debug.argtypes = [ctypes.c_int]
+    lib.pfkv_set_debug.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def set_debug(on: bool) -> bool:
+    """Switch the library's debug mode (a device-side precondition check before
+    every launch; synchronizing, not for graph capture). Returns the previous setting."""
+    return bool(load_library().pfkv_set_debug(1 if on else 0))
 
 
 def _raise_on(status: int):

@@ -22,8 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpfkv.so")
 
-SOURCES = ["pfkv_host.cpp", "splitkv_main.hip", "segment_reduce.hip", "stream_read.hip"]
-KERNEL_SOURCES = ["splitkv_main.hip", "segment_reduce.hip", "stream_read.hip"]
+SOURCES = ["pfkv_host.cpp", "splitkv_main.hip", "segment_reduce.hip", "stream_read.hip", "debug_check.hip"]
+KERNEL_SOURCES = ["splitkv_main.hip", "segment_reduce.hip", "stream_read.hip", "debug_check.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled for all device code.

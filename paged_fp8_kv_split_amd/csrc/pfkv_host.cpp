@@ -11,6 +11,7 @@
 // entry points do.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -57,6 +58,63 @@ int cached_props(int device, DeviceProps* out) {
   }
   *out = d;
   return PFKV_OK;
+}
+
+// Debug mode (PFKV_DEBUG=1 in the environment, or pfkv_set_debug): a checking
+// kernel validates the device-side inputs before every main-kernel launch. It
+// synchronizes the stream and keeps a 16-byte status buffer per device, so it
+// is not for graph capture.
+std::mutex g_debug_mu;
+int g_debug = -1;   // -1: not read from the environment yet
+std::vector<int32_t*> g_debug_status;
+
+bool debug_enabled() {
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  if (g_debug < 0) {
+    const char* e = std::getenv("PFKV_DEBUG");
+    g_debug = (e != nullptr && std::strcmp(e, "1") == 0) ? 1 : 0;
+  }
+  return g_debug == 1;
+}
+
+int debug_check(const pfkv_args* a, void* stream) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  int32_t* status = nullptr;
+  if (e == hipSuccess) {
+    std::lock_guard<std::mutex> lock(g_debug_mu);
+    if ((size_t)device >= g_debug_status.size()) g_debug_status.resize(device + 1, nullptr);
+    if (g_debug_status[device] == nullptr) e = hipMalloc((void**)&g_debug_status[device], 4 * sizeof(int32_t));
+    status = g_debug_status[device];
+  }
+  const int32_t init[4] = {0, INT32_MAX, 0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(status, init, sizeof(init), hipMemcpyHostToDevice, (hipStream_t)stream);
+  pfkv::CheckParams c;
+  c.cu_seqlens_q = a->cu_seqlens_q;
+  c.seq_lens = a->seq_lens;
+  c.block_tables = a->block_tables;
+  c.block_table_stride = a->block_table_stride;
+  c.num_seqs = a->num_seqs;
+  c.total_q = a->total_q;
+  c.max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
+  c.page_size = a->page_size;
+  c.max_pages_per_seq = a->max_pages_per_seq;
+  c.num_pages = a->num_pages;
+  if (e == hipSuccess) e = pfkv::launch_precondition_check(c, status, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  int32_t got[4] = {0, 0, 0, 0};
+  if (e == hipSuccess) e = hipMemcpy(got, status, sizeof(got), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("debug check: ") + hipGetErrorString(e));
+  }
+  if (got[0] == 0) return PFKV_OK;
+  std::string msg = "debug check: sequence " + std::to_string(got[1]) + " (value " + std::to_string(got[2]) + "):";
+  if (got[0] & 1) msg += " cu_seqlens_q does not start at 0, decreases, or does not end at total_q;";
+  if (got[0] & 2) msg += " more query tokens than max_q_len;";
+  if (got[0] & 4) msg += " seq_len below its query tokens or above page_size * max_pages_per_seq;";
+  if (got[0] & 8) msg += " block-table entry outside [0, num_pages);";
+  return fail(PFKV_INVALID, msg);
 }
 
 bool is_gfx950(const char* arch) {
@@ -312,10 +370,18 @@ int launch_reduce(const pfkv::ReduceParams& rp, void* stream) {
 
 extern "C" {
 
+int pfkv_set_debug(int on) {
+  const int prev = debug_enabled() ? 1 : 0;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  g_debug = on ? 1 : 0;
+  return prev;
+}
+
 int pfkv_verify_attn_fwd(const pfkv_args* a, void* stream) {
   pfkv::MainParams mp;
   pfkv::ReduceParams rp;
   int st = prepare(a, &mp, &rp);
+  if (st == PFKV_OK && debug_enabled()) st = debug_check(a, stream);
   if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
   if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);   // one segment: out is final
   return st;
@@ -325,6 +391,7 @@ int pfkv_splitkv_main(const pfkv_args* a, void* stream) {
   pfkv::MainParams mp;
   pfkv::ReduceParams rp;
   int st = prepare(a, &mp, &rp);
+  if (st == PFKV_OK && debug_enabled()) st = debug_check(a, stream);
   if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
   return st;
 }

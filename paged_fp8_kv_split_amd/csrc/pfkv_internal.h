@@ -74,7 +74,17 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Debug-mode precondition check of the device-side inputs.
+struct CheckParams {
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int64_t block_table_stride;
+  int32_t num_seqs, total_q, max_q_len, page_size, max_pages_per_seq, num_pages;
+};
+
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
+hipError_t launch_precondition_check(const CheckParams& p, int32_t* status, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,
                               int64_t num_pages, uint32_t* sink, hipStream_t stream);
