@@ -11,7 +11,8 @@ query heads on 1 KV head, head_dim 256, fp8 e4m3 page-16 NHD K/V, 16 segments,
 16 replicas. Prints one JSON line on stdout; progress goes to stderr.
 
 The timed region is exactly --steps back-to-back calls between two HIP events on
-the launch stream, after --warmup untimed calls. A second pass of the same
+the launch stream, after --warmup untimed calls; events after every 64 calls
+also give the median over whole rounds of 64. A second pass of the same
 length launches only the main kernel, back to back between two HIP events on
 that stream, for its average duration in the roofline. The streaming-read
 ceiling and the CPU oracle (on a bounded sample) are measured in the same run.
@@ -22,6 +23,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -34,6 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 # The pages' gfx950 assembly kernel + reduce on this workload: 67 us per call,
 # i.e. 286.72 MB / 67 us = 4.28 TB/s under the same bytes / time formula.
 PAGES_TBPS = 286.72e6 / 67e-6 / 1e12
+# calls per timing round for the median-of-rounds figure
+ROUND = 64
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "splitkv_main_prod_counters.json")
 # precision name -> (C ABI value, dtype text)
 PRECISIONS = {
@@ -197,20 +201,30 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly --steps calls
+    # Extra events every ROUND calls split the same region into rounds (no sync
+    # between them), for the median-of-rounds figure beside the whole-region mean.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = []
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     ev0.record(stream)
     for k in range(args.steps):
         call(k)
+        if (k + 1) % ROUND == 0 and k + 1 < args.steps:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
     ev1.record(stream)
     host_s = time.perf_counter() - h0
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     us_per_call = total_ms * 1e3 / args.steps
     tbps = w.kv_bytes / (us_per_call * 1e-6) / 1e12
+    bounds = [ev0] + marks + ([ev1] if args.steps % ROUND == 0 else [])
+    rounds_us = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 / ROUND for i in range(len(bounds) - 1)]
+    median_round_us = statistics.median(rounds_us) if rounds_us else None
     log(f"{args.steps} calls: {us_per_call:.2f} us/call, {tbps:.3f} TB/s effective "
-        f"(host {host_s * 1e6 / args.steps:.1f} us/call to enqueue)")
+        f"(host {host_s * 1e6 / args.steps:.1f} us/call to enqueue); "
+        f"{len(rounds_us)} rounds of {ROUND}: median {median_round_us} us/call")
 
     # ---- main kernel alone: the same number of back-to-back main-kernel
     # launches (same replica rotation) between two events on the launch stream
@@ -284,6 +298,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(total_ms / args.steps, 5),
         "us_per_call": round(us_per_call, 2),
+        "median_round_us_per_call": round(median_round_us, 2) if median_round_us else None,
+        "rounds_us_per_call": [round(x, 2) for x in rounds_us],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tbps / PAGES_TBPS, 4) if w.name == "prod" else None,
