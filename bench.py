@@ -52,9 +52,12 @@ def log(msg):
 
 
 def kernel_source_digest():
-    path = os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", "splitkv_main.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the main kernel's sources (the templates and the 16-bit instantiation)."""
+    h = hashlib.sha256()
+    for name in ("splitkv_kernel.h", "splitkv_main.hip", "pfkv_internal.h"):
+        with open(os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_name):

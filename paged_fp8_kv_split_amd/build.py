@@ -15,6 +15,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -22,8 +23,11 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpfkv.so")
 
-SOURCES = ["pfkv_host.cpp", "splitkv_main.hip", "segment_reduce.hip", "stream_read.hip", "debug_check.hip"]
-KERNEL_SOURCES = ["splitkv_main.hip", "segment_reduce.hip", "stream_read.hip", "debug_check.hip"]
+KERNEL_SOURCES = ["splitkv_main.hip", "splitkv_main_fp8p.hip", "splitkv_main_fp8.hip", "segment_reduce.hip",
+                  "stream_read.hip", "debug_check.hip"]
+SOURCES = ["pfkv_host.cpp", *KERNEL_SOURCES]
+# headers the kernel sources include (a change to one rebuilds everything anyway)
+HEADERS = ["pfkv_internal.h", "splitkv_kernel.h"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled for all device code.
@@ -74,19 +78,27 @@ def check_device_asm(asm: str, source: str) -> None:
 
 
 def build(verbose: bool = False, check: bool = True) -> str:
-    """Compile every HIP source into ``libpfkv.so``; returns its path."""
+    """Compile every HIP source into ``libpfkv.so``; returns its path.
+
+    Each source compiles to an object (and, for the check, to device assembly)
+    in parallel; the objects are then linked.
+    """
     hipcc = _hipcc()
     fd, tmp = tempfile.mkstemp(prefix="libpfkv.", suffix=".so.tmp", dir=HERE)
     os.close(fd)
     try:
-        srcs = [os.path.join(CSRC, s) for s in SOURCES]
-        _run([hipcc, *FLAGS, "-shared", "-o", tmp, *srcs], verbose)
-        if check:
-            with tempfile.TemporaryDirectory() as td:
+        with tempfile.TemporaryDirectory() as td:
+            jobs = [[hipcc, *FLAGS, "-c", "-o", os.path.join(td, s + ".o"), os.path.join(CSRC, s)] for s in SOURCES]
+            if check:
+                jobs += [[hipcc, *FLAGS, "--cuda-device-only", "-S", "-o", os.path.join(td, s + ".s"),
+                          os.path.join(CSRC, s)] for s in KERNEL_SOURCES]
+            workers = max(1, min(len(jobs), os.cpu_count() or 4, 16))
+            with ThreadPoolExecutor(workers) as pool:
+                list(pool.map(lambda cmd: _run(cmd, verbose), jobs))
+            _run([hipcc, *FLAGS, "-shared", "-o", tmp, *[os.path.join(td, s + ".o") for s in SOURCES]], verbose)
+            if check:
                 for s in KERNEL_SOURCES:
-                    out = os.path.join(td, s + ".s")
-                    _run([hipcc, *FLAGS, "--cuda-device-only", "-S", "-o", out, os.path.join(CSRC, s)], verbose)
-                    with open(out) as f:
+                    with open(os.path.join(td, s + ".s")) as f:
                         check_device_asm(f.read(), s)
         os.replace(tmp, LIB)
     finally:

@@ -84,6 +84,9 @@ struct CheckParams {
 };
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
+// the e4m3-P and e4m3-Q/P modes, one translation unit each
+hipError_t launch_splitkv_main_fp8p(const MainParams& p, int group, hipStream_t stream);
+hipError_t launch_splitkv_main_fp8(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_precondition_check(const CheckParams& p, int32_t* status, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,

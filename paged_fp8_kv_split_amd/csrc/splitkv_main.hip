@@ -1,1111 +1,15 @@
-// Split-KV main kernel for verify attention over a paged fp8 KV cache (gfx950).
-//
-// What it computes follows aiter PR #5190 ("gfx950 assembly MTP-verify attention
-// for head_dim 256 fp8 paged KV"), sections Modifications and Kernel notes: one
-// work-group per (KV segment, sequence, KV head), partial softmax statistics per
-// segment to a workspace, empty segments written neutrally, descales read from
-// device pointers. In-kernel q_len 1..4 follows SGLang PR #37465, Modifications.
-// The decomposition is this library's own:
-//
-// * 8 waves per work-group (one work-group per CU), in two roles. A step covers
-//   4 pages (64 keys); page slot j of a step belongs to waves j and j + 4, which
-//   share a SIMD.
-//   - Score wave j (waves 0-3) streams the K block of its page HBM -> LDS,
-//     converts it once and scores its 16 keys against all G * q_len (<= 64)
-//     stacked query rows, with Q held in registers; it then forms the softmax
-//     numerators P of those keys.
-//   - P.V wave j (waves 4-7) streams the V block of its page and accumulates
-//     O[:, 64 j .. 64 j + 63] += P V over all 64 keys of a step.
-//   The two waves of a SIMD are in different phases of their work, so one
-//   feeds the matrix core while the other converts or exponentiates.
-// * One work-group barrier per phase. In phase t (between barriers t and t + 1)
-//   the score waves form P of step t - 1 and compute the scores of step t; the
-//   P.V waves accumulate step t - 2. A step's scores stay in registers across
-//   one barrier, so every score wave knows, before forming P, whether any of
-//   them saw a row pass its threshold (below).
-// * K/V pages move with global_load_lds_dwordx4 (1 KiB contiguous per
-//   instruction) issued from inline asm, so the compiler does not serialise LDS
-//   reads behind every outstanding transfer. K and V have rings of their own
-//   (4 stages each); each runs three steps ahead of its consumer, with explicit
-//   vmcnt waits. Page ids are staged in LDS windows by 4-byte LDS transfers.
-// * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K converts exactly from e4m3fn to
-//   bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), Q stays bf16. The score layout
-//   puts one query row per lane column.
-// * Online softmax in the log2 domain with a lazy reference max m per row: m
-//   moves only when a row's running max exceeds it by more than 8, so
-//   P = 2^(s - m) <= 2^8 fits fp16 and the accumulator is rescaled rarely. A
-//   score wave that sees a row pass m + 8 raises its flag; in the next phase, if
-//   any flag is up, all waves take one extra barrier while the score waves
-//   exchange the step's row maxima, move m where a row's maximum passed its
-//   threshold and publish the rescale factors for the P.V waves. Rows that did
-//   not pass keep m and get bit-identical P, so each row's arithmetic depends
-//   only on that row.
-// * P is rounded to fp16 once; the same values feed the row sum l and P V.
-// * O += P V on v_mfma_f32_16x16x32_f16. V's transposed operand comes from
-//   ds_read_b64_tr_b8 and converts exactly to fp16.
-#include <type_traits>
-
-#include "pfkv_internal.h"
+// Split-KV main kernel: the 16-bit arithmetic mode (bf16 Q x bf16 K, fp16
+// P x fp16 V) and the dispatch over the three modes.
+#include "splitkv_kernel.h"
 
 namespace pfkv {
-namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-typedef __attribute__((address_space(4))) const float const_f32;
-
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kPagesPerStep = 4;                       // one page slot per score wave
-constexpr int kStages = 4;                             // depth of the K ring and of the V ring (steps)
-constexpr int kPageBytes = kPageSize * kHeadDim;       // one (page, head) block of K or V: 4 KiB
-constexpr int kStageBytes = kPagesPerStep * kPageBytes;       // K (or V) of one step: 16 KiB
-constexpr int kDmaPerWave = kPageBytes / 1024;         // 4 x 1 KiB per wave per step
-constexpr int kVDims = kHeadDim / kPagesPerStep;       // 64 output dims per P.V wave
-constexpr float kLazySlack = 8.0f;                     // log2 units
-// arithmetic modes (the C ABI's precision values)
-constexpr int kMode16 = 0;      // bf16 Q x bf16 K, fp16 P x fp16 V
-constexpr int kModeFp8P = 1;    // bf16 Q x bf16 K, e4m3 P x e4m3 V
-constexpr int kModeFp8QP = 2;   // e4m3 Q x e4m3 K, e4m3 P x e4m3 V
-
-template <int G>
-struct Cfg {
-  // 16-row MFMA blocks (all rows); at least two, so that the 32-row tiles of
-  // the fp8 P.V path stay inside the P, maximum and rescale buffers
-  static constexpr int kRowBlocks = G * kMaxQLen / 16 < 2 ? 2 : (G * kMaxQLen / 16 > kMaxRows / 16 ? kMaxRows / 16 : G * kMaxQLen / 16);
-  static constexpr int kRows = kRowBlocks * 16;
-  static constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;         // fp16 P of a step: [rb][k-step][lane] x 16 B
-  static constexpr int kOffP = 0;                                  // two P buffers
-  static constexpr int kOffMx = kOffP + 2 * kPBytes;               // step row maxima [row][slot] (slow path)
-  static constexpr int kOffAlpha = kOffMx + kRows * kPagesPerStep * 4;   // two [row] rescale-factor buffers
-  static constexpr int kOffFlag = kOffAlpha + 2 * kRows * 4;       // two flag words, byte j from score wave j
-  static constexpr int kOffIds = kOffFlag + 64;                    // page-id windows [wave][2][64]
-  static constexpr int kOffStage = (kOffIds + kWaves * 2 * 64 * 4 + 1023) & ~1023;   // K ring, then V ring
-  static constexpr int kLdsBytes = kOffStage + 2 * kStages * kStageBytes;
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][256]
-  static_assert((kPagesPerStep + 1) * kRows * 4 <= kOffObuf, "epilogue row sums and sink terms");
-  static_assert(kOffObuf + kRows * kHeadDim * 2 <= kLdsBytes, "epilogue o staging");
-};
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One 1 KiB HBM -> LDS transfer: lane i moves 16 bytes from sbase + voff to
-// LDS address lds + 16 i. M0 carries the LDS base; it is saved and restored.
-__device__ __forceinline__ void dma_1k(const uint8_t* sbase, unsigned voff, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-// As dma_1k with 4 bytes per lane: lane i moves sbase + voff to lds + 4 i.
-__device__ __forceinline__ void dma_4b(const void* sbase, unsigned voff, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-// Wait until at most `pending` of this wave's vector-memory operations are in
-// flight (0, 4, 8, 12 or 16). Inside the main loop the only such operations
-// are the page transfers (four 1 KiB transfers per wave and step) and the
-// page-id window refills, which are older than the transfers they precede.
-__device__ __forceinline__ void wait_vm(int pending) {
-  if (pending >= 16)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (pending >= 12)
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if (pending >= 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (pending >= 4)
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// Work-group barrier that orders LDS traffic but does not wait for the page
-// transfers still in flight (a __syncthreads() fence would drain vmcnt).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned lo, unsigned hi) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ f16x8 fp8x8_to_f16(unsigned lo, unsigned hi) {
-  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Geometry of one work-group's (segment, sequence, KV head), uniform.
-struct Geo {
-  int seg, b, h;     // h: this work-group's group of G query heads (query heads h G .. h G + G - 1)
-  int hkv;           // the KV head those query heads read
-  int q0, q_len, L, pb, pe, rows, n_steps;   // q0, q_len: this work-group's query tokens
-  int qoff;          // KV position of the work-group's first query token
-  int win;           // left window (clamped to L), -1 when none
-  float c2;          // k_descale * softmax_scale * log2(e): raw score -> log2 units
-};
-
-// One wave's stream of one page slot (K or V blocks) into its LDS ring: the
-// block of page slot `slot` of step t goes to ring stage t % 4.
-struct PageStream {
-  const uint8_t* cache;
-  const int32_t* bt_row;      // this sequence's block-table row
-  uint64_t page_stride;       // bytes between pages of the cache
-  unsigned goff[4];           // per-lane source offsets inside a (page, head) block
-  unsigned ring;              // LDS address of this slot in stage 0
-  unsigned ids_lds;           // this wave's two page-id windows
-  const int* ids;
-  int pb, pe, slot, n_steps, num_pages;
-  int rlog;                   // log2(cache page size / 16)
-  int next_id;                // block-table entry of the next transfer (read from LDS)
-
-  // In LDS, the 16-byte chunk at position pos of key row k (page slot j) holds
-  // dim chunk pos ^ sw(k, j), sw(k, j) = (k ^ 12 (j & 1)) & 15: K row reads and
-  // V transposed reads are then free of bank conflicts.
-  __device__ void init(const MainParams& p, const Geo& geo, uint8_t* smem, int wave, int slot_, int lane,
-                       const uint8_t* cache_, unsigned ring_stage0, int off_ids) {
-    cache = cache_;
-    bt_row = p.block_tables + (int64_t)geo.b * p.block_table_stride;
-    page_stride = (uint64_t)kPageSize * p.num_kv_heads * kHeadDim;
-    slot = slot_;
-    pb = geo.pb;
-    pe = geo.pe;
-    n_steps = geo.n_steps;
-    num_pages = p.num_pages;
-    rlog = p.page_ratio_log2;
-    const int g = lane >> 4, n = lane & 15, jpar = slot & 1;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int k = 4 * jj + g;
-      goff[jj] = (unsigned)((k * p.num_kv_heads + geo.hkv) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
-    }
-    ring = ring_stage0 + slot * kPageBytes;
-    ids_lds = lds_addr(smem + off_ids) + wave * (2 * 64 * 4);
-    ids = (const int*)(smem + off_ids) + wave * (2 * 64);
-    next_id = 0;
-  }
-  __device__ bool has(int t) const { return t < n_steps && pb + kPagesPerStep * t + slot < pe; }
-  __device__ int count(int t) const { return has(t) ? kDmaPerWave : 0; }
-  // Pages here are 16-token blocks. A cache page of 16 R tokens (R = 2^rlog)
-  // holds R of them back to back in NHD order, so 16-token block pidx is part
-  // pidx mod R of cache page block_tables[pidx / R], at 16-token index
-  // block_tables[pidx / R] R + pidx mod R.
-  // Entry k of window w (w even / odd in two slots) is the table entry of step 64 w + k.
-  __device__ void fetch_window(int win, int lane) {
-    int pidx = pb + kPagesPerStep * (64 * win + lane) + slot;
-    pidx = pidx < pe ? pidx : pb;                      // lanes past the segment read a valid entry
-    dma_4b(bt_row, (unsigned)(4 * (pidx >> rlog)), ids_lds + (win & 1) * 256);
-  }
-  // 16-token block of step t from its table entry (clamped into the cache first)
-  __device__ int resolve(int t, int entry) const {
-    const int id = min(max(entry, 0), num_pages - 1);
-    return (id << rlog) + ((pb + kPagesPerStep * t + slot) & ((1 << rlog) - 1));
-  }
-  __device__ int read_id(int t) const { return ids[((t >> 6) & 1) * 64 + (t & 63)]; }
-  __device__ int first_id(int t) const {            // scalar load, before the windows land
-    return ((const const_i32*)bt_row)[(has(t) ? pb + kPagesPerStep * t + slot : pb) >> rlog];
-  }
-  __device__ void put(int t, int entry) {
-    const int id = resolve(t, entry);
-    const uint8_t* base = cache + (uint64_t)id * page_stride;
-    const unsigned dst = ring + (t % kStages) * kStageBytes;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
-  }
-  // the transfer of step t; window w + 1 is fetched while window w is half used
-  __device__ void issue(int t, int lane) {
-    if (has(t)) {
-      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
-      put(t, __builtin_amdgcn_readfirstlane(next_id));
-      next_id = read_id(t + 1);
-    }
-  }
-  // The same transfer in four parts that the caller spreads over its work:
-  // begin() resolves the page (and refills the window when due), part(q, jj)
-  // moves the jj-th KiB.
-  struct Pending {
-    const uint8_t* base;
-    unsigned dst;
-    bool on;
-  };
-  __device__ Pending begin(int t, int lane) {
-    Pending q{nullptr, 0u, has(t)};
-    if (q.on) {
-      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
-      const int id = resolve(t, __builtin_amdgcn_readfirstlane(next_id));
-      q.base = cache + (uint64_t)id * page_stride;
-      q.dst = ring + (t % kStages) * kStageBytes;
-      next_id = read_id(t + 1);
-    }
-    return q;
-  }
-  __device__ void part(const Pending& q, int jj) const {
-    if (q.on) dma_1k(q.base, goff[jj], q.dst + 1024 * jj);
-  }
-};
-
-// Stores the staged 16-bit rows ([row][256] in LDS) of the work-group, all
-// 512 threads: fp16 o rows to the workspace with 16-byte streaming stores, or,
-// with a single segment, the final bf16 rows to out with 8-byte stores (out
-// rows are 8-byte aligned).
-template <int G>
-__device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
-  if (p.direct) {
-    for (int idx = threadIdx.x; idx < geo.rows * 64; idx += kThreads) {
-      const int row = idx >> 6, c = idx & 63;
-      const int i = row / G, gg = row - (row / G) * G;
-      uint16_t* dst = p.out + (int64_t)(geo.q0 + i) * p.out_stride_token + (int64_t)(geo.h * G + gg) * p.out_stride_head + 4 * c;
-      *(uint2*)dst = *(const uint2*)(obuf + row * 512 + 8 * c);
-    }
-    return;
-  }
-  const int T = p.total_q, Hq = p.num_q_heads;
-  for (int idx = threadIdx.x; idx < geo.rows * 32; idx += kThreads) {
-    const int row = idx >> 5, c = idx & 31;
-    const int i = row / G, gg = row - (row / G) * G;
-    uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + geo.q0 + i) * Hq + geo.h * G + gg) * kHeadDim + 8 * c;
-    __builtin_nontemporal_store(*(const u32x4*)(obuf + row * 512 + 16 * c), (u32x4*)dst);
-  }
-}
-
-// fp8 (e4m3fn) MFMA with unit block scales (E8M0 127 = 2^0) on both operands
-__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
-  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-// Score wave w (page slot w): K stream, S^T = K Q^T for all NRB row blocks,
-// lazy softmax, P to LDS, row sums; writes m and l of the segment. With F8,
-// Q is quantised per row to e4m3 (scale amax / 448, folded into that row's
-// score multiplier), S^T runs on the fp8 MFMA and P is rounded to e4m3.
-template <int G, int NRB, int MODE>
-__device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
-  using C = Cfg<G>;
-  constexpr bool F8 = MODE == kModeFp8QP;    // e4m3 Q, S^T on the fp8 MFMA
-  constexpr bool F8P = MODE != kMode16;      // e4m3 P
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int h = geo.h, q0 = geo.q0, q_len = geo.q_len, L = geo.L, pb = geo.pb;
-  const int rows = geo.rows, n_steps = geo.n_steps;
-  const float c2 = geo.c2;
-  // left window: the first step of a segment that starts below the largest
-  // lower key bound (that of the last query row) masks keys from below
-  const int win = geo.win;
-  const int qoff = geo.qoff;
-  const bool win_head = win >= 0 && kPageSize * pb < qoff + q_len - 1 - win;
-  const bool capped = p.softcap > 0.f;
-  uint8_t* const k_ring = smem + C::kOffStage;
-
-  PageStream ks;   // K of page slot w: streamed by P.V wave w + 4, read here
-  ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
-
-  // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
-  // phase 1) by page-style transfers, 16-byte chunk c of row r at position
-  // c ^ (r & 15), score wave w moving rows 16w..16w+15, while the P.V waves
-  // start the K and V streams. Q moves to registers after the first barrier.
-  uint8_t* const q_stage = smem + C::kOffStage + (kStages + 2) * kStageBytes;
-  if (n_steps > 0) {
-    if (w < NRB) {
-      const uint8_t* q_base = (const uint8_t*)(p.q + (int64_t)q0 * p.q_stride_token + (int64_t)h * G * p.q_stride_head);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 16 * w + 2 * k + (lane >> 5);
-        const int rr = r < rows ? r : 0;            // padding rows read row 0, zeroed in registers
-        const int i = rr / G, gg = rr - (rr / G) * G;
-        const unsigned voff = (unsigned)((i * p.q_stride_token + gg * p.q_stride_head) * 2) + 16u * ((lane & 31) ^ (r & 15));
-        dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + 2 * k) * 512);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
-  // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
-  // With F8 (q8): byte b of k-step ks holds dim 128 ks + 32 g + b, and c2r is
-  // the row's score multiplier c2 * amax / 448.
-  bf16x8 qop[F8 ? 1 : NRB][4][2];
-  i32x8 q8[F8 ? NRB : 1][2];
-  float c2r[NRB], inv_c2r[NRB];
-  float cap_a[NRB], cap_b[NRB];   // soft-cap in raw-score units: s -> cap_b tanh(cap_a s)
-  auto load_q = [&]() {
-    if constexpr (F8) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int r = 16 * rb + n;
-        const bool pad = r >= rows;
-        bf16x8 x[2][4];
-        float amax = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const int pos = (16 * ks + 4 * g + c4) ^ n;
-            const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
-            x[ks][c4] = pad ? bf16x8{} : v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[ks][c4][e]));
-          }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;   // q8 = e4m3(q * qs)
-        c2r[rb] = c2 / qs;
-        inv_c2r[rb] = 1.0f / c2r[rb];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const bf16x8& xv = x[ks][d >> 1];
-            const int e = 4 * (d & 1);
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e] * qs, (float)xv[e + 1] * qs, 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e + 2] * qs, (float)xv[e + 3] * qs, word, true);
-            q8[rb][ks][d] = word;
-          }
-      }
-      return;
-    }
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      c2r[rb] = c2;
-      inv_c2r[rb] = 1.0f / c2;
-      const int r = 16 * rb + n;
-      const bool pad = r >= rows;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int pos = (8 * u + 2 * g + hh) ^ n;
-          const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
-          qop[rb][u][hh] = pad ? bf16x8{} : v;
-        }
-    }
-  };
-
-  // ---- per-lane LDS addresses
-  // K of key n: bf16 path chunks 4u + g (u = 0..3); fp8 path chunks 2g, 2g+1
-  // (k-step 0) and 8 + 2g, 9 + 2g (k-step 1); a chunk c sits at c ^ sw
-  const unsigned ksw = (unsigned)((n ^ (12 * (w & 1))) & 15);
-  unsigned k_off[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const unsigned c = F8 ? (unsigned)(2 * g + (u & 1) + 8 * (u >> 1)) : (unsigned)(4 * u + g);
-    k_off[u] = C::kOffStage + w * kPageBytes + 256 * n + 16u * (c ^ ksw);
-  }
-  // P of row 16 rb + n, keys 4g..4g+3 of slot w: half (w & 1) of the 16-byte
-  // A operand of lane (g, n) in k-step w >> 1
-  const int p_off = C::kOffP + ((w >> 1) * 64 + lane) * 16 + (w & 1) * 8;
-  // fp8 P: row-major [row][64 keys], 16-key chunk (page slot) w of row r at
-  // position w ^ ((r >> 2) & 3); this lane writes keys 4g..4g+3
-  auto p8_off = [&](int rb) { const int r = 16 * rb + n; return C::kOffP + r * 64 + 16 * (w ^ ((r >> 2) & 3)) + 4 * g; };
-  float* const mx = (float*)(smem + C::kOffMx);
-  float* const alpha_buf = (float*)(smem + C::kOffAlpha);
-
-  f32x4 sv[NRB];            // raw scores of the current step: lane (g, n) key 4g + r, row 16 rb + n
-  float m_ref[NRB];         // reference max (log2 units) of row 16 rb + n, identical in every score wave
-  float thr[NRB];           // raw-score threshold (m + slack) / c2r
-  float l_lane[NRB];        // this lane's share of the row sums
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    m_ref[rb] = -__builtin_inff();
-    thr[rb] = -__builtin_inff();
-    l_lane[rb] = 0.f;
-  }
-
-  // raw scores of this wave's page of step t from its K block (kraw, read
-  // from LDS by the caller). In tail steps the page may be missing and keys
-  // past a row's causal limit (or the sequence end) are masked to -inf;
-  // steady-state steps need neither.
-  auto score_step = [&](int t, const u32x4 (&kraw)[4], auto tail) {
-    constexpr bool kTail = decltype(tail)::value;
-    const int pidx = pb + kPagesPerStep * t + w;
-    if (!kTail || ks.has(t)) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) sv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (F8) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const i32x8 ka = cat8(kraw[2 * ks], kraw[2 * ks + 1]);
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) sv[rb] = mfma_fp8_16x16x128(ka, q8[rb][ks], sv[rb]);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 k0 = fp8x8_to_bf16(kraw[u][0], kraw[u][1]);
-          const bf16x8 k1 = fp8x8_to_bf16(kraw[u][2], kraw[u][3]);
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) {
-            sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rb][u][0], sv[rb], 0, 0, 0);
-            sv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[rb][u][1], sv[rb], 0, 0, 0);
-          }
-        }
-      }
-      if (capped) {
-        // s -> cap tanh(s / cap) in the row's raw-score units; tanh y =
-        // 1 - 2 / (1 + e^(2y)), which saturates to +-1 without overflow
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(2.88539008177792681f * cap_a[rb] * sv[rb][r]);
-            sv[rb][r] = cap_b[rb] * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
-          }
-      }
-      if (kTail && (kPageSize * (pidx + 1) > qoff + 1 || (win >= 0 && kPageSize * pidx < qoff + q_len - 1 - win))) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const int i = (16 * rb + n) / G;
-          const int lim = min(L - 1, qoff + i);
-          const int lo = win < 0 ? 0 : qoff + i - win;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kPageSize * pidx + 4 * g + r;
-            sv[rb][r] = (key <= lim && key >= lo) ? sv[rb][r] : -__builtin_inff();
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) sv[rb] = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-    }
-  };
-
-  // P of step u (scores in sv). P is first formed against the current m,
-  // while the flag word (any score wave saw a row pass its threshold in step
-  // u) is still in flight; in the rare slow path it is formed again.
-  auto form_p = [&](int u, int pbuf, unsigned flag_word) {
-    f32x4 pv[NRB];
-    auto exps = [&]() {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2r[rb], -mref));
-      }
-    };
-    exps();
-    if (__builtin_amdgcn_readfirstlane(flag_word) != 0) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float v = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
-        if (g == 0) mx[(16 * rb + n) * kPagesPerStep + w] = v;
-      }
-      lds_barrier();   // the P.V waves take this barrier too
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const f32x4 m4 = *(const f32x4*)(mx + (16 * rb + n) * kPagesPerStep);
-        const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        float alpha = 1.f;
-        if (M > thr[rb]) {
-          const float m_new = M * c2r[rb];
-          alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);   // 0 when m was -inf
-          m_ref[rb] = m_new;
-          thr[rb] = (m_new + kLazySlack) * inv_c2r[rb];
-        }
-        l_lane[rb] *= alpha;
-        if (w == 0 && g == 0) alpha_buf[(u & 1) * C::kRows + 16 * rb + n] = alpha;
-      }
-      exps();
-    }
-    if constexpr (F8P) {
-      // e4m3 P (round to nearest even); l sums the rounded values
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][0], pv[rb][1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][2], pv[rb][3], word, true);
-        *(int*)(smem + p8_off(rb) + pbuf * C::kPBytes) = word;
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        l_lane[rb] += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-      }
-    } else {
-      const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const f16x4 ph = {(_Float16)pv[rb][0], (_Float16)pv[rb][1], (_Float16)pv[rb][2], (_Float16)pv[rb][3]};
-        *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = ph;
-        const f16x2 lo = {ph[0], ph[1]}, hi = {ph[2], ph[3]};
-        l_lane[rb] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[rb], false), false);
-      }
-    }
-  };
-
-  // Phase t: P of step t-1, scores and flag of step t, barrier. The LDS reads of the phase (flag word,
-  // K block) are issued first. Steady-state phases (4 <= t, t + 4 < n_steps)
-  // have full steps t..t+3, no masking, and the ring stage ST = t % 4 as a
-  // compile-time constant.
-  auto phase = [&](int t, auto tail, auto stage) {
-    constexpr bool kTail = decltype(tail)::value;
-    constexpr int kSt = decltype(stage)::value;
-    const int kst = kSt >= 0 ? kSt : (t & 3);
-    const bool have_p = !kTail || (t >= 1 && t <= n_steps);
-    const bool have_s = !kTail || t < n_steps;
-    unsigned flag_word = 0;
-    if (have_p) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((kst + 3) & 1));
-    u32x4 kraw[4];
-    if (!kTail || ks.has(t)) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kraw[u] = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
-    }
-    if (have_p) form_p(t - 1, (kst + 3) & 1, flag_word);
-    if (have_s) {
-      if (kTail && (t + 2 >= n_steps || (t == 0 && win_head)))
-        score_step(t, kraw, std::true_type{});
-      else
-        score_step(t, kraw, std::false_type{});
-      bool over = false;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) over |= sv[rb][r] > thr[rb];
-      const bool any = __any(over);
-      if (lane == 0) smem[C::kOffFlag + 4 * (kst & 1) + w] = any ? 1 : 0;
-    }
-    lds_barrier();   // the P.V waves have waited for K of step t+1
-  };
-
-  if (n_steps > 0) {
-    lds_barrier();   // Q and step 0's K are in LDS
-    load_q();
-    if (capped) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        cap_a[rb] = c2r[rb] * 0.69314718055994531f / p.softcap;
-        cap_b[rb] = 1.f / cap_a[rb];
-      }
-    }
-    int t = 0;
-    for (; t < 4 && t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
-    for (; t + 7 < n_steps; t += 4) {
-      phase(t, std::false_type{}, std::integral_constant<int, 0>{});
-      phase(t + 1, std::false_type{}, std::integral_constant<int, 1>{});
-      phase(t + 2, std::false_type{}, std::integral_constant<int, 2>{});
-      phase(t + 3, std::false_type{}, std::integral_constant<int, 3>{});
-    }
-    for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
-  }
-
-  // ---- segment partials. The loop's last barrier has retired every LDS
-  // access and transfer. l of a row sums the page slots' key subsets in a
-  // fixed order (score and P.V waves alike); m is identical in every score
-  // wave. The P.V waves divide their accumulators by l and stage fp16 o in LDS
-  // for full-row stores.
-  float* const lsum = (float*)smem;   // [slot][row]
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    float l = l_lane[rb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (g == 0) lsum[w * C::kRows + 16 * rb + n] = l;
-    // one segment with sink logits: the sink's share of the denominator,
-    // 2^(sink - m), joins the row sums as a fifth slot for the P.V waves
-    if (g == 0 && w == 0 && p.direct && p.sinks != nullptr) {
-      const int row = 16 * rb + n;
-      const int gg = (row < rows ? row : 0) % G;
-      const float sink2 = ((const const_f32*)p.sinks)[h * G + gg] * 1.44269504088896341f;
-      lsum[kPagesPerStep * C::kRows + row] = __builtin_amdgcn_exp2f(sink2 - m_ref[rb]);
-    }
-  }
-  lds_barrier();   // row sums of every page slot
-  if (w == 0 && g == 0 && (!p.direct || p.lse != nullptr)) {
-    const int T = p.total_q, Hq = p.num_q_heads;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int row = 16 * rb + n;
-      if (row < rows) {
-        float l = lsum[row];
-#pragma unroll
-        for (int v = 1; v < kPagesPerStep; ++v) l += lsum[v * C::kRows + row];
-        const int i = row / G, gg = row - (row / G) * G;
-        if (p.direct) {
-          // one segment: the row's log-sum-exp goes straight to lse (natural
-          // log), a sink logit joining the sum as 2^(sink - mx), mx = max(m, sink)
-          float mx = m_ref[rb], den = l;
-          if (p.sinks != nullptr) {
-            const float sink2 = ((const const_f32*)p.sinks)[h * G + gg] * 1.44269504088896341f;
-            mx = fmaxf(m_ref[rb], sink2);
-            den = (m_ref[rb] == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(m_ref[rb] - mx)) +
-                  __builtin_amdgcn_exp2f(sink2 - mx);
-          }
-          p.lse[(int64_t)(h * G + gg) * T + q0 + i] =
-              den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
-        } else {
-          float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
-          // streaming stores: the partials are read once, by the reduce
-          __builtin_nontemporal_store(m_ref[rb], dst);
-          __builtin_nontemporal_store(l, dst + 1);
-        }
-      }
-    }
-  }
-  lds_barrier();   // o staged
-  store_rows<G>(p, geo, smem + C::kOffObuf);
-}
-
-// P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
-// NRB row blocks; stages its slice of the segment's normalised output o. With
-// F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
-// e4m3 bytes.
-template <int G, int NRB, int MODE>
-__device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
-  using C = Cfg<G>;
-  constexpr bool F8 = MODE != kMode16;       // e4m3 P and V on the fp8 MFMA
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int v = w - 4;
-  const int lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int h = geo.h, q0 = geo.q0, L = geo.L, pb = geo.pb, pe = geo.pe;
-  const int rows = geo.rows, n_steps = geo.n_steps;
-  uint8_t* const k_ring = smem + C::kOffStage;
-  uint8_t* const v_ring = k_ring + kStages * kStageBytes;
-
-  // Both blocks of page slot v stream through this wave: K (page-id windows
-  // in the slot of score wave v, which streams nothing) three steps ahead of
-  // its use by the score waves, V three steps ahead of its use here.
-  PageStream ks, vs;
-  ks.init(p, geo, smem, v, v, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
-  vs.init(p, geo, smem, w, v, lane, p.v_cache, lds_addr(v_ring), C::kOffIds);
-  if (n_steps > 0) {
-    ks.fetch_window(0, lane);
-    vs.fetch_window(0, lane);
-    const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
-    if (ks.has(0)) ks.put(0, id0);
-    if (ks.has(1)) ks.put(1, id1);
-    if (ks.has(2)) ks.put(2, id2);
-    if (vs.has(0)) vs.put(0, id0);
-    wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // the windows and K of step 0
-    ks.next_id = ks.read_id(3);
-    vs.next_id = vs.read_id(1);
-  }
-
-  // V^T operand: source lane n of group g supplies the 8 dims at +8 (n & 1) of
-  // key 4g + ((n >> 1) & 3) in page slot 2 ks + (n >> 3), the k-slot (n >> 1)
-  // of group g; ds_read_b64_tr_b8 hands lane n byte k of source lane 2k + n/8.
-  const int vpar = (n >> 3) & 1;
-  const int vkey = 4 * g + ((n >> 1) & 3);
-  const unsigned vsw = 16u * ((vkey ^ (12 * vpar)) & 15);
-  unsigned v_off[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    v_off[db] = C::kOffStage + kStages * kStageBytes + vpar * kPageBytes + 256 * vkey + 8 * (n & 1) +
-                ((unsigned)(kVDims * v + 16 * db) ^ vsw);
-  const int p_off = C::kOffP + lane * 16;
-  const float* const alpha_buf = (const float*)(smem + C::kOffAlpha);
-
-  // fp8 path. Lane l of a 32x32x64 tile: A (P) row 32 rt + (l & 31) with keys
-  // 32 q .. 32 q + 31 (q = l >> 5) of the step as bytes 0..31; B (V) dim
-  // 32 dt + (l & 31) of this wave's 64 with the same keys, gathered by four
-  // ds_read_b64_tr_b8 of 8 keys each: in its 16-lane group, source lane
-  // 2k + hb supplies the 8 dims at +8 hb of key 32 q + 8 j + k.
-  constexpr int NRT = (NRB + 1) / 2;    // 32-row tiles
-  unsigned v8_off[F8 ? 2 : 1][4];
-  int p8_rd[F8 ? NRT : 1];
-  if constexpr (F8) {
-    const int q = lane >> 5, sub = (lane >> 4) & 1, src = lane & 15, kk8 = src >> 1, hb = src & 1;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int slot = 2 * q + (j >> 1), kin = 8 * (j & 1) + kk8;
-        const unsigned chunk = (unsigned)(4 * v + 2 * dt + sub);
-        const unsigned sw = (unsigned)((kin ^ (12 * (slot & 1))) & 15);
-        v8_off[dt][j] = C::kOffStage + kStages * kStageBytes + slot * kPageBytes + 256 * kin + 16u * (chunk ^ sw) + 8 * hb;
-      }
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int r = 32 * rt + (lane & 31);
-      p8_rd[rt] = C::kOffP + r * 64 + 16 * ((2 * q) ^ ((r >> 2) & 3));   // chunk 2q; chunk 2q+1 at ^1
-    }
-  }
-
-  f32x4 acc[F8 ? 1 : NRB][4];
-  f32x16 acc8[F8 ? NRT : 1][2];
-  if constexpr (F8) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) acc8[rt][dt] = f32x16{};
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  bool slow1 = false;   // flag of step t-1 in phase t
-  bool slow2 = false;   // flag of step t-2 in phase t
-
-  // Phase t: the LDS reads of step t-2 (V block, P) and of the flag word of
-  // step t-1 first; an extra barrier if step t-1 takes the slow path; the V
-  // transfer of step t+1; O += P V of step t-2 (rescaled first if step t-2
-  // moved m); wait for V of step t-1; barrier.
-  auto phase = [&](int t, auto tail, auto stage) {
-    constexpr bool kTail = decltype(tail)::value;
-    constexpr int kSt = decltype(stage)::value;
-    const bool have_f = !kTail || (t >= 1 && t <= n_steps);
-    const bool have_pv = !kTail || (t >= 2 && t - 2 < n_steps);
-    const int u = t - 2;
-    const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
-    const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
-    // K of step t+3 and V of step t+1: eight 1 KiB parts, spread over the
-    // MFMA groups below so that a part that waits for room in the memory
-    // pipeline does not hold up the whole phase's arithmetic
-    const PageStream::Pending kq = ks.begin(t + 3, lane);
-    const PageStream::Pending vq = vs.begin(t + 1, lane);
-    auto parts = [&](int d0, int d1) {
-      __builtin_amdgcn_sched_barrier(0);
-      for (int d = d0; d < d1; ++d) {
-        if (d < 4)
-          ks.part(kq, d);
-        else
-          vs.part(vq, d - 4);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    unsigned flag_word = 0;
-    if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
-    // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
-    i32x2 vraw[2][4];
-    f16x8 pa[F8 ? 1 : NRB][2];
-    i32x8 pa8[F8 ? NRT : 1];
-    if (F8 && have_pv) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vraw[dt][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + v8_off[dt][j] + vst * kStageBytes));
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const uint8_t* pr = smem + p8_rd[rt] + pbuf * C::kPBytes;
-        pa8[rt] = cat8(*(const u32x4*)pr, *(const u32x4*)(smem + ((p8_rd[rt] + pbuf * C::kPBytes) ^ 16)));
-      }
-    }
-    if (!F8 && have_pv) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          vraw[kk][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)(smem + v_off[db] + vst * kStageBytes + kk * 2 * kPageBytes));
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          pa[rb][kk] = *(const f16x8*)(smem + p_off + pbuf * C::kPBytes + (rb * 2 + kk) * (64 * 16));
-    }
-    slow2 = slow1;
-    slow1 = have_f && __builtin_amdgcn_readfirstlane(flag_word) != 0;
-    if (slow1) lds_barrier();   // matches the score waves' maxima exchange
-    if (F8 && have_pv) {
-      if constexpr (kTail) {
-        // keys past the segment or the sequence end: V bytes 0
-        if (u == n_steps - 1) {
-          const int q = lane >> 5;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int page = pb + kPagesPerStep * u + 2 * q + (j >> 1);
-            unsigned lo = 0, hi = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const int key = kPageSize * page + 8 * (j & 1) + k;
-              const unsigned m8 = (page < pe && key < L) ? 0xffu : 0u;
-              if (k < 4) lo |= m8 << (8 * k); else hi |= m8 << (8 * (k - 4));
-            }
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-              vraw[dt][j][0] &= (int)lo;
-              vraw[dt][j][1] &= (int)hi;
-            }
-          }
-        }
-      }
-      if (slow2) {
-        // rows 32 rt + 8 c + 4 (lane >> 5) + e hold acc8[rt][dt][4 c + e]
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 32 * rt + 8 * c + 4 * (lane >> 5));
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc8[rt][dt][4 * c + e] *= a[e];
-          }
-      }
-      i32x8 vb[2];
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        vb[dt] = i32x8{vraw[dt][0][0], vraw[dt][0][1], vraw[dt][1][0], vraw[dt][1][1],
-                       vraw[dt][2][0], vraw[dt][2][1], vraw[dt][3][0], vraw[dt][3][1]};
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
-          const int gi = rt * 2 + dt;
-          parts(8 * gi / (2 * NRT), 8 * (gi + 1) / (2 * NRT));
-        }
-    } else if (!F8 && have_pv) {
-      f16x8 vf[2][4];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) vf[kk][db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
-      if constexpr (kTail) {
-        // keys of pages past the segment (never loaded: stale or uninitialised
-        // LDS) and past the sequence end get V = 0, so P = 0 never meets a NaN
-        if (u == n_steps - 1) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int page = pb + kPagesPerStep * u + 2 * kk + (e >> 2);
-              const int key = kPageSize * page + 4 * g + (e & 3);
-              const bool keep = page < pe && key < L;
-#pragma unroll
-              for (int db = 0; db < 4; ++db) vf[kk][db][e] = keep ? vf[kk][db][e] : (_Float16)0.f;
-            }
-        }
-      }
-      if (slow2) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 16 * rb + 4 * g);
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rb][db][r] *= a[r];
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-            acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
-          const int gi = kk * NRB + rb;
-          parts(8 * gi / (2 * NRB), 8 * (gi + 1) / (2 * NRB));
-        }
-    } else {
-      parts(0, 8);
-    }
-    // K of step t+1 and V of step t-1 (issued in phase t-2) must have landed;
-    // the transfers of phases t-1 and t may fly
-    if constexpr (kTail)
-      wait_vm(ks.count(t + 2) + vs.count(t) + ks.count(t + 3) + vs.count(t + 1));
-    else
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    lds_barrier();
-  };
-
-  if (n_steps > 0) {
-    lds_barrier();
-    int t = 0;
-    for (; t < 4 && t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
-    for (; t + 7 < n_steps; t += 4) {
-      phase(t, std::false_type{}, std::integral_constant<int, 0>{});
-      phase(t + 1, std::false_type{}, std::integral_constant<int, 1>{});
-      phase(t + 2, std::false_type{}, std::integral_constant<int, 2>{});
-      phase(t + 3, std::false_type{}, std::integral_constant<int, 3>{});
-    }
-    for (; t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
-  }
-
-  lds_barrier();   // the score waves' row sums of every page slot
-  const float* const lsum = (const float*)smem;
-  _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
-  uint16_t* const obuf_bits = (uint16_t*)obuf;
-  const float vd = p.direct ? *(const const_f32*)p.v_descale : 1.f;
-  if constexpr (F8) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < rows) {
-          float l = lsum[row];
-#pragma unroll
-          for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
-          if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
-          const float inv = l > 0.f ? vd / l : 0.f;
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const int at = row * kHeadDim + kVDims * v + 32 * dt + (lane & 31);
-            if (p.direct)
-              obuf_bits[at] = (uint16_t)bf16_rne(acc8[rt][dt][r] * inv);
-            else
-              obuf[at] = (_Float16)(acc8[rt][dt][r] * inv);
-          }
-        }
-      }
-  } else {
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * rb + 4 * g + r;
-      if (row < rows) {
-        float l = lsum[row];
-#pragma unroll
-        for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
-        if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
-        // o = acc / l (0 with no visible key); a single segment writes out = vd o
-        const float inv = l > 0.f ? vd / l : 0.f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int at = row * kHeadDim + kVDims * v + 16 * db + n;
-          if (p.direct)
-            obuf_bits[at] = (uint16_t)bf16_rne(acc[rb][db][r] * inv);
-          else
-            obuf[at] = (_Float16)(acc[rb][db][r] * inv);
-        }
-      }
-    }
-  }
-  lds_barrier();
-  store_rows<G>(p, geo, smem + C::kOffObuf);
-}
-
-template <int G, int NRB, int MODE>
-__device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
-  if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB, MODE>(p, geo, smem);
-  else
-    pv_wave<G, NRB, MODE>(p, geo, smem);
-}
-
-template <int G, int MODE>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-splitkv_main_kernel(MainParams p) {
-  using C = Cfg<G>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
-
-  const const_i32* cu = (const const_i32*)p.cu_seqlens_q;
-  const const_i32* sl = (const const_i32*)p.seq_lens;
-  Geo geo;
-  geo.seg = blockIdx.x;
-  geo.b = blockIdx.y;
-  geo.h = blockIdx.z / p.q_split;
-  geo.hkv = geo.h / p.kv_split;
-  // out-of-contract values are clamped so that every access stays in its buffer
-  const int seq_q0 = cu[geo.b];
-  int seq_qlen = cu[geo.b + 1] - seq_q0;
-  if (seq_q0 < 0 || seq_q0 >= p.total_q) seq_qlen = 0;
-  seq_qlen = min(max(seq_qlen, 0), min(kMaxQLen, p.total_q - max(seq_q0, 0)));
-  // this work-group's block of the sequence's query tokens
-  const int i0 = (blockIdx.z % p.q_split) * p.q_per_wg;
-  const int q_len = min(seq_qlen - i0, p.q_per_wg);
-  if (q_len <= 0) return;
-  geo.q0 = seq_q0 + i0;
-  geo.q_len = q_len;
-  geo.L = min(max(sl[geo.b], 0), p.max_pages_per_seq * kPageSize);
-  geo.qoff = geo.L - seq_qlen + i0;
-  const int pages = (geo.L + kPageSize - 1) / kPageSize;
-  // with a left window the segments split only the pages some query can see;
-  // the first page is bounded with the largest q_len, so that the partition,
-  // and with it every row's bits, does not depend on the call's q_len
-  geo.win = p.window_left < 0 ? -1 : min(p.window_left, geo.L);
-  const int first = geo.win < 0 ? 0 : min(max(geo.L - kMaxQLen - geo.win, 0) / kPageSize, pages);
-  const int span = pages - first;
-  const int chunk = (span + p.num_segments - 1) / p.num_segments;
-  geo.pb = first + min(geo.seg * chunk, span);
-  geo.pe = first + min(geo.seg * chunk + chunk, span);
-  geo.rows = G * q_len;
-  geo.n_steps = (geo.pe - geo.pb + kPagesPerStep - 1) / kPagesPerStep;
-  geo.c2 = *(const const_f32*)p.k_descale * p.score_scale_log2;
-
-  const int nrb = (geo.rows + 15) >> 4;
-  if constexpr (G == 16) {
-    switch (nrb) {
-      case 1: verify_segment<16, 1, MODE>(p, geo, smem); break;
-      case 2: verify_segment<16, 2, MODE>(p, geo, smem); break;
-      case 3: verify_segment<16, 3, MODE>(p, geo, smem); break;
-      default: verify_segment<16, 4, MODE>(p, geo, smem); break;
-    }
-  } else if constexpr (G == 8) {
-    switch (nrb) {
-      case 1: verify_segment<8, 1, MODE>(p, geo, smem); break;
-      case 2: verify_segment<8, 2, MODE>(p, geo, smem); break;
-      case 3: verify_segment<8, 3, MODE>(p, geo, smem); break;
-      default: verify_segment<8, 4, MODE>(p, geo, smem); break;
-    }
-  } else {
-    if (nrb == 1)
-      verify_segment<4, 1, MODE>(p, geo, smem);
-    else
-      verify_segment<4, 2, MODE>(p, geo, smem);
-  }
-}
-
-// group: query heads per work-group (16, 8 or 4; 32 query heads per KV head run
-// as two 16-head work-groups, p.kv_split = 2)
-template <int MODE>
-hipError_t launch_mode(const MainParams& p, int group, hipStream_t stream) {
-  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
-  if (group == 16)
-    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 8)
-    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 4)
-    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-}  // namespace
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream) {
   if (p.kv_split != 1 && !(p.kv_split == 2 && group == 16)) return hipErrorInvalidValue;
   switch (p.precision) {
     case kMode16: return launch_mode<kMode16>(p, group, stream);
-    case kModeFp8P: return launch_mode<kModeFp8P>(p, group, stream);
-    case kModeFp8QP: return launch_mode<kModeFp8QP>(p, group, stream);
+    case kModeFp8P: return launch_splitkv_main_fp8p(p, group, stream);
+    case kModeFp8QP: return launch_splitkv_main_fp8(p, group, stream);
     default: return hipErrorInvalidValue;
   }
 }
