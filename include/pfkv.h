@@ -10,7 +10,8 @@
  * to the first L_b positions of the paged fp8 KV cache, query i (0-based) seeing
  * positions 0 .. L_b - n_b + i (a causal mask over the last n_b positions). The
  * cache is NHD with 16-token pages (also 32 or 64 here: a page of 16 R tokens is
- * R 16-token blocks back to back) and head_dim 256; K and V are e4m3fn bytes
+ * R 16-token blocks back to back; and one-token pages, where every key row is
+ * gathered through its own block-table entry) and head_dim 256; K and V are e4m3fn bytes
  * whose real values are byte * k_descale (resp. v_descale); G = Hq / Hkv query
  * heads share each KV head, query head hq reading KV head hq / G. The pages'
  * kernel serves G = 16 and 8 (aiter PR #5190, Supported); this library also
@@ -68,7 +69,7 @@ typedef struct pfkv_args {
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
   int32_t head_dim;            /* must be 256 */
-  int32_t page_size;           /* 16 (the pages' kernel), 32 or 64 */
+  int32_t page_size;           /* 16 (the pages' kernel), 32, 64 or 1 (one table entry per token) */
   int32_t num_pages;           /* pages in k_cache / v_cache */
   int32_t max_pages_per_seq;   /* columns of block_tables that may be read */
   int32_t num_segments;        /* S in [1, 64] */

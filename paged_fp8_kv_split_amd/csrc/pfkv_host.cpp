@@ -223,12 +223,14 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   // Supported envelope of the kernels.
   if (!is_gfx950(arch)) return fail(PFKV_UNSUPPORTED, std::string("device is ") + arch + ", kernels are gfx950");
   if (a->head_dim != pfkv::kHeadDim) return fail(PFKV_UNSUPPORTED, "head_dim must be 256");
-  if (a->page_size != 16 && a->page_size != 32 && a->page_size != 64)
-    return fail(PFKV_UNSUPPORTED, "page_size must be 16, 32 or 64");
-  if ((int64_t)a->max_pages_per_seq * (a->page_size / pfkv::kPageSize) > (1 << 26))
-    return fail(PFKV_INVALID, "max_pages_per_seq * page_size / 16 must be <= 2^26");
-  if ((int64_t)a->num_pages * (a->page_size / pfkv::kPageSize) > INT32_MAX)
-    return fail(PFKV_INVALID, "num_pages * page_size / 16 must fit in int32");
+  if (a->page_size != 1 && a->page_size != 16 && a->page_size != 32 && a->page_size != 64)
+    return fail(PFKV_UNSUPPORTED, "page_size must be 1, 16, 32 or 64");
+  if (a->page_size > 1) {
+    if ((int64_t)a->max_pages_per_seq * (a->page_size / pfkv::kPageSize) > (1 << 26))
+      return fail(PFKV_INVALID, "max_pages_per_seq * page_size / 16 must be <= 2^26");
+    if ((int64_t)a->num_pages * (a->page_size / pfkv::kPageSize) > INT32_MAX)
+      return fail(PFKV_INVALID, "num_pages * page_size / 16 must fit in int32");
+  }
   const int group = a->num_q_heads / a->num_kv_heads;
   if (group != 32 && group != 16 && group != 8 && group != 4)
     return fail(PFKV_UNSUPPORTED, "query heads per KV head must be 32, 16, 8 or 4, got " + std::to_string(group));
@@ -328,7 +330,8 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.num_kv_heads = a->num_kv_heads;
   m.num_pages = a->num_pages;
   m.page_ratio_log2 = a->page_size == 64 ? 2 : (a->page_size == 32 ? 1 : 0);
-  m.max_pages_per_seq = a->max_pages_per_seq << m.page_ratio_log2;   // in 16-token blocks
+  m.token_pages = a->page_size == 1 ? 1 : 0;
+  m.max_seq_len = a->max_pages_per_seq * a->page_size;   // <= 2^30 (checked)
   m.num_segments = a->num_segments;
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
 

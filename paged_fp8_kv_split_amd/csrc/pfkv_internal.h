@@ -48,11 +48,13 @@ struct MainParams {
   // q_per_wg tokens (kMaxRows / G); q_split = 2 when a sequence may have more
   // (blockIdx.z = head_group * q_split + block)
   int32_t q_split, q_per_wg;
-  // cache pages of 16 << page_ratio_log2 tokens; num_pages counts cache pages,
-  // max_pages_per_seq counts 16-token blocks
+  // cache pages of 16 << page_ratio_log2 tokens, or of one token when
+  // token_pages (page_ratio_log2 = 0 then); num_pages counts cache pages
   int32_t page_ratio_log2;
+  int32_t token_pages;
+  int32_t max_seq_len;         // max_pages_per_seq * page_size: bound on seq_lens
   int32_t precision;           // 0: 16-bit Q/P, 1: e4m3 P, 2: e4m3 Q (per-row scale) and P
-  int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, num_segments;
+  int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
 };
 

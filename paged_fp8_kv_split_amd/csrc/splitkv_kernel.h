@@ -62,6 +62,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -119,6 +120,20 @@ __device__ __forceinline__ void dma_1k(const uint8_t* sbase, unsigned voff, unsi
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// As dma_1k with a 64-bit source address per lane (lane i moves addr_i).
+__device__ __forceinline__ void dma_1k_addr(const uint8_t* addr, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(addr), "s"(lds)
       : "memory");
 }
 
@@ -187,19 +202,35 @@ struct Geo {
   float c2;          // k_descale * softmax_scale * log2(e): raw score -> log2 units
 };
 
+// Table entries behind one transfer: with cache pages of 16 or more tokens, one
+// entry, uniform over the wave; with one-token pages, this lane's four entries
+// (tokens 4 jj + g of the 16-token block, jj = 0..3, g = lane / 16).
+template <bool TOK>
+struct PageIds {
+  using type = int;
+};
+template <>
+struct PageIds<true> {
+  using type = i32x4;
+};
+
 // One wave's stream of one page slot (K or V blocks) into its LDS ring: the
-// block of page slot `slot` of step t goes to ring stage t % 4.
+// 16-token block of page slot `slot` of step t goes to ring stage t % 4.
+// TOK: the cache has one-token pages, so each key row of a block is gathered
+// from its own page (a 1 KiB transfer then covers four rows of 256 bytes).
+template <bool TOK>
 struct PageStream {
+  using Ids = typename PageIds<TOK>::type;
   const uint8_t* cache;
   const int32_t* bt_row;      // this sequence's block-table row
-  uint64_t page_stride;       // bytes between pages of the cache
-  unsigned goff[4];           // per-lane source offsets inside a (page, head) block
+  uint64_t page_stride;       // bytes between 16-token blocks (TOK: between tokens) of the cache
+  unsigned goff[4];           // per-lane source offsets inside a block (TOK: inside a token's page)
   unsigned ring;              // LDS address of this slot in stage 0
   unsigned ids_lds;           // this wave's two page-id windows
   const int* ids;
-  int pb, pe, slot, n_steps, num_pages;
+  int pb, pe, slot, n_steps, num_pages, L, lane4;
   int rlog;                   // log2(cache page size / 16)
-  int next_id;                // block-table entry of the next transfer (read from LDS)
+  Ids next_id;                // table entries of the next transfer (read from LDS)
 
   // In LDS, the 16-byte chunk at position pos of key row k (page slot j) holds
   // dim chunk pos ^ sw(k, j), sw(k, j) = (k ^ 12 (j & 1)) & 15: K row reads and
@@ -208,23 +239,25 @@ struct PageStream {
                        const uint8_t* cache_, unsigned ring_stage0, int off_ids) {
     cache = cache_;
     bt_row = p.block_tables + (int64_t)geo.b * p.block_table_stride;
-    page_stride = (uint64_t)kPageSize * p.num_kv_heads * kHeadDim;
+    page_stride = (uint64_t)(TOK ? 1 : kPageSize) * p.num_kv_heads * kHeadDim;
     slot = slot_;
     pb = geo.pb;
     pe = geo.pe;
     n_steps = geo.n_steps;
     num_pages = p.num_pages;
+    L = geo.L;
     rlog = p.page_ratio_log2;
     const int g = lane >> 4, n = lane & 15, jpar = slot & 1;
+    lane4 = 4 * g;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int k = 4 * jj + g;
-      goff[jj] = (unsigned)((k * p.num_kv_heads + geo.hkv) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
+      goff[jj] = (unsigned)(((TOK ? 0 : k * p.num_kv_heads) + geo.hkv) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
     }
     ring = ring_stage0 + slot * kPageBytes;
     ids_lds = lds_addr(smem + off_ids) + wave * (2 * 64 * 4);
     ids = (const int*)(smem + off_ids) + wave * (2 * 64);
-    next_id = 0;
+    next_id = Ids{};
   }
   __device__ bool has(int t) const { return t < n_steps && pb + kPagesPerStep * t + slot < pe; }
   __device__ int count(int t) const { return has(t) ? kDmaPerWave : 0; }
@@ -232,57 +265,92 @@ struct PageStream {
   // holds R of them back to back in NHD order, so 16-token block pidx is part
   // pidx mod R of cache page block_tables[pidx / R], at 16-token index
   // block_tables[pidx / R] R + pidx mod R.
-  // Entry k of window w (w even / odd in two slots) is the table entry of step 64 w + k.
+  // Windows (two slots, w even / odd): with 16 R-token pages entry k of window
+  // w is the table entry of step 64 w + k; with one-token pages, window w
+  // covers steps 4 w .. 4 w + 3 and entry 16 s + 4 g + jj holds token 4 jj + g
+  // of step 4 w + s (a lane's four entries are adjacent). Tokens past the
+  // sequence end read the last token's entry, so no unused entry is read.
   __device__ void fetch_window(int win, int lane) {
-    int pidx = pb + kPagesPerStep * (64 * win + lane) + slot;
-    pidx = pidx < pe ? pidx : pb;                      // lanes past the segment read a valid entry
-    dma_4b(bt_row, (unsigned)(4 * (pidx >> rlog)), ids_lds + (win & 1) * 256);
+    if constexpr (TOK) {
+      const int s = lane >> 4, gg = (lane >> 2) & 3, jj = lane & 3;
+      int pidx = pb + kPagesPerStep * (4 * win + s) + slot;
+      pidx = pidx < pe ? pidx : pb;
+      const int tok = min(kPageSize * pidx + 4 * jj + gg, L - 1);
+      dma_4b(bt_row, (unsigned)(4 * tok), ids_lds + (win & 1) * 256);
+    } else {
+      int pidx = pb + kPagesPerStep * (64 * win + lane) + slot;
+      pidx = pidx < pe ? pidx : pb;                    // lanes past the segment read a valid entry
+      dma_4b(bt_row, (unsigned)(4 * (pidx >> rlog)), ids_lds + (win & 1) * 256);
+    }
+  }
+  // the next window is fetched at the step that starts (TOK) or half uses the
+  // current one; it lands at least three phases before its first use
+  __device__ void refill(int t, int lane) {
+    if constexpr (TOK) {
+      if ((t & 3) == 0 && t + 4 < n_steps) fetch_window((t >> 2) + 1, lane);
+    } else {
+      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
+    }
   }
   // 16-token block of step t from its table entry (clamped into the cache first)
   __device__ int resolve(int t, int entry) const {
     const int id = min(max(entry, 0), num_pages - 1);
     return (id << rlog) + ((pb + kPagesPerStep * t + slot) & ((1 << rlog) - 1));
   }
-  __device__ int read_id(int t) const { return ids[((t >> 6) & 1) * 64 + (t & 63)]; }
+  __device__ Ids read_id(int t) const {
+    if constexpr (TOK)
+      return *(const i32x4*)(ids + ((t >> 2) & 1) * 64 + (t & 3) * 16 + lane4);
+    else
+      return ids[((t >> 6) & 1) * 64 + (t & 63)];
+  }
   __device__ int first_id(int t) const {            // scalar load, before the windows land
     return ((const const_i32*)bt_row)[(has(t) ? pb + kPagesPerStep * t + slot : pb) >> rlog];
   }
-  __device__ void put(int t, int entry) {
-    const int id = resolve(t, entry);
-    const uint8_t* base = cache + (uint64_t)id * page_stride;
-    const unsigned dst = ring + (t % kStages) * kStageBytes;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
+  // TOK: source of part jj (this lane's token 4 jj + g), its page clamped into the cache
+  __device__ const uint8_t* token_src(const i32x4& e, int jj) const {
+    const int id = min(max(e[jj], 0), num_pages - 1);
+    return cache + (uint64_t)id * page_stride + goff[jj];
   }
-  // the transfer of step t; window w + 1 is fetched while window w is half used
-  __device__ void issue(int t, int lane) {
-    if (has(t)) {
-      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
-      put(t, __builtin_amdgcn_readfirstlane(next_id));
-      next_id = read_id(t + 1);
+  __device__ void put(int t, const Ids& entry) {
+    const unsigned dst = ring + (t % kStages) * kStageBytes;
+    if constexpr (TOK) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_1k_addr(token_src(entry, jj), dst + 1024 * jj);
+    } else {
+      const uint8_t* base = cache + (uint64_t)resolve(t, entry) * page_stride;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
     }
   }
-  // The same transfer in four parts that the caller spreads over its work:
-  // begin() resolves the page (and refills the window when due), part(q, jj)
-  // moves the jj-th KiB.
+  // The transfer of step t in four parts that the caller spreads over its
+  // work: begin() resolves the page (and refills the window when due),
+  // part(q, jj) moves the jj-th KiB.
   struct Pending {
     const uint8_t* base;
     unsigned dst;
     bool on;
+    Ids e;
   };
   __device__ Pending begin(int t, int lane) {
-    Pending q{nullptr, 0u, has(t)};
+    Pending q{nullptr, 0u, has(t), Ids{}};
     if (q.on) {
-      if ((t & 63) == 32 && t + 32 < n_steps) fetch_window((t >> 6) + 1, lane);
-      const int id = resolve(t, __builtin_amdgcn_readfirstlane(next_id));
-      q.base = cache + (uint64_t)id * page_stride;
+      refill(t, lane);
+      if constexpr (TOK)
+        q.e = next_id;
+      else
+        q.base = cache + (uint64_t)resolve(t, __builtin_amdgcn_readfirstlane(next_id)) * page_stride;
       q.dst = ring + (t % kStages) * kStageBytes;
       next_id = read_id(t + 1);
     }
     return q;
   }
   __device__ void part(const Pending& q, int jj) const {
-    if (q.on) dma_1k(q.base, goff[jj], q.dst + 1024 * jj);
+    if (q.on) {
+      if constexpr (TOK)
+        dma_1k_addr(token_src(q.e, jj), q.dst + 1024 * jj);
+      else
+        dma_1k(q.base, goff[jj], q.dst + 1024 * jj);
+    }
   }
 };
 
@@ -325,7 +393,7 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // lazy softmax, P to LDS, row sums; writes m and l of the segment. With F8,
 // Q is quantised per row to e4m3 (scale amax / 448, folded into that row's
 // score multiplier), S^T runs on the fp8 MFMA and P is rounded to e4m3.
-template <int G, int NRB, int MODE>
+template <int G, int NRB, int MODE, bool TOK>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G>;
   constexpr bool F8 = MODE == kModeFp8QP;    // e4m3 Q, S^T on the fp8 MFMA
@@ -344,7 +412,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   const bool capped = p.softcap > 0.f;
   uint8_t* const k_ring = smem + C::kOffStage;
 
-  PageStream ks;   // K of page slot w: streamed by P.V wave w + 4, read here
+  PageStream<TOK> ks;   // K of page slot w: streamed by P.V wave w + 4, read here
   ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
 
   // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
@@ -694,7 +762,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 // NRB row blocks; stages its slice of the segment's normalised output o. With
 // F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
 // e4m3 bytes.
-template <int G, int NRB, int MODE>
+template <int G, int NRB, int MODE, bool TOK>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G>;
   constexpr bool F8 = MODE != kMode16;       // e4m3 P and V on the fp8 MFMA
@@ -710,18 +778,34 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   // Both blocks of page slot v stream through this wave: K (page-id windows
   // in the slot of score wave v, which streams nothing) three steps ahead of
   // its use by the score waves, V three steps ahead of its use here.
-  PageStream ks, vs;
+  PageStream<TOK> ks, vs;
   ks.init(p, geo, smem, v, v, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
   vs.init(p, geo, smem, w, v, lane, p.v_cache, lds_addr(v_ring), C::kOffIds);
   if (n_steps > 0) {
     ks.fetch_window(0, lane);
     vs.fetch_window(0, lane);
-    const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
-    if (ks.has(0)) ks.put(0, id0);
-    if (ks.has(1)) ks.put(1, id1);
-    if (ks.has(2)) ks.put(2, id2);
-    if (vs.has(0)) vs.put(0, id0);
-    wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // the windows and K of step 0
+    if constexpr (TOK) {
+      // one-token pages: the entries come from the windows (steps 0..3 in
+      // window 0; window 1, due at step 4, is fetched here too)
+      if (4 < n_steps) {
+        ks.fetch_window(1, lane);
+        vs.fetch_window(1, lane);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const i32x4 id0 = ks.read_id(0), id1 = ks.read_id(1), id2 = ks.read_id(2);
+      if (ks.has(0)) ks.put(0, id0);
+      if (ks.has(1)) ks.put(1, id1);
+      if (ks.has(2)) ks.put(2, id2);
+      if (vs.has(0)) vs.put(0, id0);
+      wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // K of step 0
+    } else {
+      const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
+      if (ks.has(0)) ks.put(0, id0);
+      if (ks.has(1)) ks.put(1, id1);
+      if (ks.has(2)) ks.put(2, id2);
+      if (vs.has(0)) vs.put(0, id0);
+      wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // the windows and K of step 0
+    }
     ks.next_id = ks.read_id(3);
     vs.next_id = vs.read_id(1);
   }
@@ -798,8 +882,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     // K of step t+3 and V of step t+1: eight 1 KiB parts, spread over the
     // MFMA groups below so that a part that waits for room in the memory
     // pipeline does not hold up the whole phase's arithmetic
-    const PageStream::Pending kq = ks.begin(t + 3, lane);
-    const PageStream::Pending vq = vs.begin(t + 1, lane);
+    const typename PageStream<TOK>::Pending kq = ks.begin(t + 3, lane);
+    const typename PageStream<TOK>::Pending vq = vs.begin(t + 1, lane);
     auto parts = [&](int d0, int d1) {
       __builtin_amdgcn_sched_barrier(0);
       for (int d = d0; d < d1; ++d) {
@@ -1015,15 +1099,16 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   store_rows<G>(p, geo, smem + C::kOffObuf);
 }
 
-template <int G, int NRB, int MODE>
+template <int G, int NRB, int MODE, bool TOK>
 __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
   if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB, MODE>(p, geo, smem);
+    score_wave<G, NRB, MODE, TOK>(p, geo, smem);
   else
-    pv_wave<G, NRB, MODE>(p, geo, smem);
+    pv_wave<G, NRB, MODE, TOK>(p, geo, smem);
 }
 
-template <int G, int MODE>
+// TOK: the cache has one-token pages
+template <int G, int MODE, bool TOK>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
   using C = Cfg<G>;
@@ -1047,7 +1132,7 @@ splitkv_main_kernel(MainParams p) {
   if (q_len <= 0) return;
   geo.q0 = seq_q0 + i0;
   geo.q_len = q_len;
-  geo.L = min(max(sl[geo.b], 0), p.max_pages_per_seq * kPageSize);
+  geo.L = min(max(sl[geo.b], 0), p.max_seq_len);
   geo.qoff = geo.L - seq_qlen + i0;
   const int pages = (geo.L + kPageSize - 1) / kPageSize;
   // with a left window the segments split only the pages some query can see;
@@ -1066,40 +1151,46 @@ splitkv_main_kernel(MainParams p) {
   const int nrb = (geo.rows + 15) >> 4;
   if constexpr (G == 16) {
     switch (nrb) {
-      case 1: verify_segment<16, 1, MODE>(p, geo, smem); break;
-      case 2: verify_segment<16, 2, MODE>(p, geo, smem); break;
-      case 3: verify_segment<16, 3, MODE>(p, geo, smem); break;
-      default: verify_segment<16, 4, MODE>(p, geo, smem); break;
+      case 1: verify_segment<16, 1, MODE, TOK>(p, geo, smem); break;
+      case 2: verify_segment<16, 2, MODE, TOK>(p, geo, smem); break;
+      case 3: verify_segment<16, 3, MODE, TOK>(p, geo, smem); break;
+      default: verify_segment<16, 4, MODE, TOK>(p, geo, smem); break;
     }
   } else if constexpr (G == 8) {
     switch (nrb) {
-      case 1: verify_segment<8, 1, MODE>(p, geo, smem); break;
-      case 2: verify_segment<8, 2, MODE>(p, geo, smem); break;
-      case 3: verify_segment<8, 3, MODE>(p, geo, smem); break;
-      default: verify_segment<8, 4, MODE>(p, geo, smem); break;
+      case 1: verify_segment<8, 1, MODE, TOK>(p, geo, smem); break;
+      case 2: verify_segment<8, 2, MODE, TOK>(p, geo, smem); break;
+      case 3: verify_segment<8, 3, MODE, TOK>(p, geo, smem); break;
+      default: verify_segment<8, 4, MODE, TOK>(p, geo, smem); break;
     }
   } else {
     if (nrb == 1)
-      verify_segment<4, 1, MODE>(p, geo, smem);
+      verify_segment<4, 1, MODE, TOK>(p, geo, smem);
     else
-      verify_segment<4, 2, MODE>(p, geo, smem);
+      verify_segment<4, 2, MODE, TOK>(p, geo, smem);
   }
+}
+
+// TOK: one-token cache pages
+template <int MODE, bool TOK>
+hipError_t launch_tok(const MainParams& p, int group, hipStream_t stream) {
+  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
+  if (group == 16)
+    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+  else if (group == 8)
+    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+  else if (group == 4)
+    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // group: query heads per work-group (16, 8 or 4; 32 query heads per KV head run
 // as two 16-head work-groups, p.kv_split = 2)
 template <int MODE>
 hipError_t launch_mode(const MainParams& p, int group, hipStream_t stream) {
-  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
-  if (group == 16)
-    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 8)
-    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 4)
-    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE>), grid, dim3(kThreads), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return p.token_pages ? launch_tok<MODE, true>(p, group, stream) : launch_tok<MODE, false>(p, group, stream);
 }
 
 }  // namespace

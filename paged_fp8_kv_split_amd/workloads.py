@@ -95,6 +95,8 @@ WORKLOADS = {
                                       descale="override"),
     # production verify: 16 x 35000, GQA 16, 16 segments
     "prod": _uniform("prod", 16, 35000, 4, 16, 1, 16, seed=2, replicas=16),
+    # the production shape over one-token pages (every key row at a random slot)
+    "prod_page1": _uniform("prod_page1", 16, 35000, 4, 16, 1, 16, seed=2, replicas=16, page_size=1),
     # GQA 8
     "gqa8": _uniform("gqa8", 16, 35000, 4, 8, 1, 16, seed=3, replicas=16),
     # long context and occupancy pair

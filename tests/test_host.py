@@ -106,6 +106,8 @@ CASES = [
     ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
     ("page 32", dict(page_size=32), "gfx950", OK),
     ("page 64", dict(page_size=64), "gfx950", OK),
+    ("page 1", dict(page_size=1), "gfx950", OK),
+    ("page 2", dict(page_size=2), "gfx950", UNSUPPORTED),
     ("page 8", dict(page_size=8), "gfx950", UNSUPPORTED),
     ("page 128", dict(page_size=128), "gfx950", UNSUPPORTED),
     ("page 64 table too wide", dict(page_size=64, max_pages_per_seq=(1 << 25), block_table_stride=(1 << 25)),
