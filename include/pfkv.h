@@ -11,7 +11,8 @@
  * positions 0 .. L_b - n_b + i (a causal mask over the last n_b positions). The
  * cache is NHD with 16-token pages (also 32 or 64 here: a page of 16 R tokens is
  * R 16-token blocks back to back; and one-token pages, where every key row is
- * gathered through its own block-table entry) and head_dim 256; K and V are e4m3fn bytes
+ * gathered through its own block-table entry) and head_dim 256 (also 128 here);
+ * K and V are e4m3fn bytes
  * whose real values are byte * k_descale (resp. v_descale); G = Hq / Hkv query
  * heads share each KV head, query head hq reading KV head hq / G. The pages'
  * kernel serves G = 16 and 8 (aiter PR #5190, Supported); this library also
@@ -68,7 +69,7 @@ typedef struct pfkv_args {
   int32_t total_q;             /* T = cu_seqlens_q[N], 1 <= T <= max_q_len N */
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
-  int32_t head_dim;            /* must be 256 */
+  int32_t head_dim;            /* 256 (the pages' kernel) or 128; q, out and both caches share it */
   int32_t page_size;           /* 16 (the pages' kernel), 32, 64 or 1 (one table entry per token) */
   int32_t num_pages;           /* pages in k_cache / v_cache */
   int32_t max_pages_per_seq;   /* columns of block_tables that may be read */
@@ -194,7 +195,7 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
  * Workspace bytes for S segments: S * total_q * num_q_heads * 520. 0 for bad
  * sizes. Layout (after the main kernel): fp16 o[S][total_q][num_q_heads][256],
  * the segment's softmax-weighted mean of V (without v_descale, 0 for a segment
- * with no visible key), then fp32 (m, l)[S][total_q][num_q_heads], m the
+ * with no visible key; at head_dim 128 the first 128 of each row), then fp32 (m, l)[S][total_q][num_q_heads], m the
  * segment's reference max of the scores in log2 units (-inf when empty) and
  * l the sum of 2^(score - m) over its keys.
  */

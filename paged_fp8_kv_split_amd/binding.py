@@ -181,6 +181,8 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
         raise TypeError("k_cache / v_cache must be [num_pages, page_size, Hkv, D] of equal shape")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise TypeError("k_cache / v_cache must be contiguous")
+    if k_cache.shape[3] != q.shape[2]:
+        raise TypeError(f"k_cache / v_cache head_dim ({k_cache.shape[3]}) must equal q's ({q.shape[2]})")
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("cu_seqlens_q", cu_seqlens_q)):
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")

@@ -204,7 +204,7 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
     // max_q_len, times its query heads) with 32-bit byte offsets
     const int64_t group = a->num_q_heads / a->num_kv_heads;
     const int64_t tokens = max_q_len;
-    const int64_t span = ((tokens - 1) * a->q_stride_token + (group - 1) * a->q_stride_head + pfkv::kHeadDim) * 2;
+    const int64_t span = ((tokens - 1) * a->q_stride_token + (group - 1) * a->q_stride_head + a->head_dim) * 2;
     if (span >= ((int64_t)1 << 32)) return fail(PFKV_INVALID, "q strides too large (a KV head's rows span >= 4 GiB)");
   }
   if (a->out_stride_token % 4 || a->out_stride_head % 4 || !aligned(a->out, 8))
@@ -222,7 +222,7 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
 
   // Supported envelope of the kernels.
   if (!is_gfx950(arch)) return fail(PFKV_UNSUPPORTED, std::string("device is ") + arch + ", kernels are gfx950");
-  if (a->head_dim != pfkv::kHeadDim) return fail(PFKV_UNSUPPORTED, "head_dim must be 256");
+  if (a->head_dim != 256 && a->head_dim != 128) return fail(PFKV_UNSUPPORTED, "head_dim must be 256 or 128");
   if (a->page_size != 1 && a->page_size != 16 && a->page_size != 32 && a->page_size != 64)
     return fail(PFKV_UNSUPPORTED, "page_size must be 1, 16, 32 or 64");
   if (a->page_size > 1) {
@@ -324,6 +324,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
     m.q_split = (max_q_len + m.q_per_wg - 1) / m.q_per_wg;
   }
   m.precision = a->precision;
+  m.head_dim = a->head_dim;
   m.num_seqs = a->num_seqs;
   m.total_q = a->total_q;
   m.num_q_heads = a->num_q_heads;
@@ -346,6 +347,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   rp->total_q = a->total_q;
   rp->num_q_heads = a->num_q_heads;
   rp->num_segments = a->num_segments;
+  rp->head_dim = a->head_dim;
   (void)group;
   return PFKV_OK;
 }

@@ -6,7 +6,7 @@
 
 namespace pfkv {
 
-constexpr int kHeadDim = 256;   // head_dim served by the kernels
+constexpr int kHeadDim = 256;   // largest head_dim served (also 128); the workspace row stride
 constexpr int kPageSize = 16;   // tokens per KV page
 constexpr int kMaxQLen = 8;     // query tokens per sequence (the pages' 4, or up to 8 with max_q_len)
 constexpr int kDefaultMaxQLen = 4;
@@ -16,6 +16,7 @@ constexpr int kMaxSegments = 64;
 // Workspace layout, written by the main kernel and read by the reduce:
 //   o  [S][T][Hq][256] fp16  the segment's softmax-weighted mean of V (V without
 //                            its descale): sum p V / sum p, 0 when sum p = 0
+//                            (head dim 128: the first 128 of each row's 256)
 //   ml [S][T][Hq][2]   fp32  (m, l): reference max in log2 units and l = sum p
 // so that segment s contributes  2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
 constexpr int kPartialBytes = kHeadDim * 2 + 2 * 4;   // workspace bytes per (segment, token, head)
@@ -54,6 +55,7 @@ struct MainParams {
   int32_t token_pages;
   int32_t max_seq_len;         // max_pages_per_seq * page_size: bound on seq_lens
   int32_t precision;           // 0: 16-bit Q/P, 1: e4m3 P, 2: e4m3 Q (per-row scale) and P
+  int32_t head_dim;            // 256 or 128
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
 };
@@ -67,6 +69,7 @@ struct ReduceParams {
   float* lse;                  // optional [Hq][T] fp32
   const float* sinks;          // optional [Hq] fp32 sink logits
   int32_t total_q, num_q_heads, num_segments;
+  int32_t head_dim;            // 256 or 128 (o rows keep the kHeadDim stride)
 };
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
@@ -86,9 +89,11 @@ struct CheckParams {
 };
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
-// the e4m3-P and e4m3-Q/P modes, one translation unit each
+// the e4m3-P and e4m3-Q/P modes at head dim 256, and every mode at head dim
+// 128, one translation unit each
 hipError_t launch_splitkv_main_fp8p(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_splitkv_main_fp8(const MainParams& p, int group, hipStream_t stream);
+hipError_t launch_splitkv_main_hd128(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_precondition_check(const CheckParams& p, int32_t* status, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,

@@ -13,8 +13,9 @@
 // statistics (aiter PR #7375, Behavior and intent). A sink logit of the row's
 // head adds e^sink to the denominator (and to the lse sum) and nothing to the
 // numerator.
-// One wave per output row: lane s holds (m_s, l_s), every lane four dims of
-// the fp16 o rows, whose loads for up to 16 segments are in flight together.
+// One wave per output row: lane s holds (m_s, l_s), lane i dims 4i .. 4i + 3
+// of the fp16 o rows (head dim 128: lanes 0-31), whose loads for up to 16
+// segments are in flight together.
 #include "pfkv_internal.h"
 
 namespace pfkv {
@@ -40,12 +41,13 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   const int S = p.num_segments;
 
   // the o loads of the first segments go out before (m, l) is known
+  const bool dims = 4 * lane < p.head_dim;   // this lane's dims exist
   const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
   const int64_t seg_stride = rows_total * kHeadDim;
   f16x4 a[kBatch];
 #pragma unroll
   for (int k = 0; k < kBatch; ++k)
-    if (k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + k * seg_stride));
+    a[k] = (k < S && dims) ? __builtin_nontemporal_load((const f16x4*)(o + k * seg_stride)) : f16x4{};
 
   float m = -__builtin_inff(), l = 0.f;
   if (lane < S) {
@@ -66,7 +68,7 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
     if (s0 > 0) {
 #pragma unroll
       for (int k = 0; k < kBatch; ++k)
-        if (s0 + k < S) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
+        if (s0 + k < S && dims) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
@@ -87,7 +89,7 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
   uint16_t* dst = p.out + t * p.out_stride_token + hq * p.out_stride_head + 4 * lane;
   const uint32_t lo = bf16_rne(num[0] * inv) | (bf16_rne(num[1] * inv) << 16);
   const uint32_t hi = bf16_rne(num[2] * inv) | (bf16_rne(num[3] * inv) << 16);
-  *(uint2*)dst = make_uint2(lo, hi);
+  if (dims) *(uint2*)dst = make_uint2(lo, hi);
   if (p.lse != nullptr && lane == 0)
     p.lse[hq * p.total_q + t] = den > 0.f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
 }

@@ -74,17 +74,34 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPagesPerStep = 4;                       // one page slot per score wave
 constexpr int kStages = 4;                             // depth of the K ring and of the V ring (steps)
-constexpr int kPageBytes = kPageSize * kHeadDim;       // one (page, head) block of K or V: 4 KiB
-constexpr int kStageBytes = kPagesPerStep * kPageBytes;       // K (or V) of one step: 16 KiB
-constexpr int kDmaPerWave = kPageBytes / 1024;         // 4 x 1 KiB per wave per step
-constexpr int kVDims = kHeadDim / kPagesPerStep;       // 64 output dims per P.V wave
 constexpr float kLazySlack = 8.0f;                     // log2 units
 // arithmetic modes (the C ABI's precision values)
 constexpr int kMode16 = 0;      // bf16 Q x bf16 K, fp16 P x fp16 V
 constexpr int kModeFp8P = 1;    // bf16 Q x bf16 K, e4m3 P x e4m3 V
 constexpr int kModeFp8QP = 2;   // e4m3 Q x e4m3 K, e4m3 P x e4m3 V
 
-template <int G>
+// Sizes that follow from the head dim D (256, or 128)
+template <int D>
+struct Dim {
+  static_assert(D == 256 || D == 128, "head dims 256 and 128");
+  static constexpr int kPageBytes = kPageSize * D;          // one (16-token block, head) of K or V: 4 / 2 KiB
+  static constexpr int kStageBytes = kPagesPerStep * kPageBytes;   // K (or V) of one step: 16 / 8 KiB
+  static constexpr int kDmaPerWave = kPageBytes / 1024;     // 1 KiB transfers per wave and step: 4 / 2
+  static constexpr int kVDims = D / kPagesPerStep;          // output dims per P.V wave: 64 / 32
+  static constexpr int kChunks = D / 16;                    // 16-byte chunks of an fp8 K/V row
+  static constexpr int kRowsPerKiB = 1024 / D;              // K/V rows per 1 KiB transfer
+  static constexpr int kKU = D / 64;                        // 16-byte K chunks a score lane reads per step
+  static constexpr int kQRowBytes = 2 * D;                  // a bf16 Q row
+  static constexpr int kQRowsPerKiB = 1024 / kQRowBytes;
+  // LDS chunk swizzle of key row k in a page slot of parity j: within 16 lanes
+  // that read one chunk of 16 rows (K rows) or 8 bytes of 8 rows in two slots
+  // (V transposed), every 16-byte (8-byte) slot of a 256-byte bank line is hit once
+  static __device__ __forceinline__ int sw(int k, int j) {
+    return D == 256 ? ((k ^ (12 * j)) & 15) : (((k >> 1) ^ (4 * j)) & 7);
+  }
+};
+
+template <int G, int D>
 struct Cfg {
   // 16-row MFMA blocks (all rows); at least two, so that the 32-row tiles of
   // the fp8 P.V path stay inside the P, maximum and rescale buffers
@@ -97,11 +114,13 @@ struct Cfg {
   static constexpr int kOffFlag = kOffAlpha + 2 * kRows * 4;       // two flag words, byte j from score wave j
   static constexpr int kOffIds = kOffFlag + 64;                    // page-id windows [wave][2][64]
   static constexpr int kOffStage = (kOffIds + kWaves * 2 * 64 * 4 + 1023) & ~1023;   // K ring, then V ring
-  static constexpr int kLdsBytes = kOffStage + 2 * kStages * kStageBytes;
+  static constexpr int kLdsBytes = kOffStage + 2 * kStages * Dim<D>::kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][256]
+  static constexpr int kOffObuf = 2048;                             // epilogue: fp16 o rows [row][D]
   static_assert((kPagesPerStep + 1) * kRows * 4 <= kOffObuf, "epilogue row sums and sink terms");
-  static_assert(kOffObuf + kRows * kHeadDim * 2 <= kLdsBytes, "epilogue o staging");
+  static_assert(kOffObuf + kRows * D * 2 <= kLdsBytes, "epilogue o staging");
+  // Q is staged in V ring stages 2-3 (unused before the first barrier)
+  static_assert(kRows * Dim<D>::kQRowBytes <= 2 * Dim<D>::kStageBytes, "Q staging");
 };
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -152,18 +171,27 @@ __device__ __forceinline__ void dma_4b(const void* sbase, unsigned voff, unsigne
 }
 
 // Wait until at most `pending` of this wave's vector-memory operations are in
-// flight (0, 4, 8, 12 or 16). Inside the main loop the only such operations
-// are the page transfers (four 1 KiB transfers per wave and step) and the
-// page-id window refills, which are older than the transfers they precede.
+// flight (rounded down to an even count, at most 16). Inside the main loop the
+// only such operations are the page transfers (kDmaPerWave 1 KiB transfers per
+// stream and step) and the page-id window refills, which are older than the
+// transfers they precede, so extra refills only make a wait stricter.
 __device__ __forceinline__ void wait_vm(int pending) {
   if (pending >= 16)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (pending >= 14)
+    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
   else if (pending >= 12)
     asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (pending >= 10)
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
   else if (pending >= 8)
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (pending >= 6)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if (pending >= 4)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (pending >= 2)
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -203,43 +231,51 @@ struct Geo {
 };
 
 // Table entries behind one transfer: with cache pages of 16 or more tokens, one
-// entry, uniform over the wave; with one-token pages, this lane's four entries
-// (tokens 4 jj + g of the 16-token block, jj = 0..3, g = lane / 16).
-template <bool TOK>
+// entry, uniform over the wave; with one-token pages, this lane's entries for
+// the rows it moves (token R jj + r of the 16-token block in part jj, R rows per
+// 1 KiB part, r = lane / (D / 16)).
+template <bool TOK, int D>
 struct PageIds {
   using type = int;
 };
 template <>
-struct PageIds<true> {
+struct PageIds<true, 256> {
   using type = i32x4;
+};
+template <>
+struct PageIds<true, 128> {
+  using type = i32x2;
 };
 
 // One wave's stream of one page slot (K or V blocks) into its LDS ring: the
 // 16-token block of page slot `slot` of step t goes to ring stage t % 4.
 // TOK: the cache has one-token pages, so each key row of a block is gathered
-// from its own page (a 1 KiB transfer then covers four rows of 256 bytes).
-template <bool TOK>
+// from its own page (a 1 KiB transfer then covers 1024 / D rows).
+template <bool TOK, int D>
 struct PageStream {
-  using Ids = typename PageIds<TOK>::type;
+  using Dm = Dim<D>;
+  using Ids = typename PageIds<TOK, D>::type;
+  static constexpr int kParts = Dm::kDmaPerWave;
   const uint8_t* cache;
   const int32_t* bt_row;      // this sequence's block-table row
   uint64_t page_stride;       // bytes between 16-token blocks (TOK: between tokens) of the cache
-  unsigned goff[4];           // per-lane source offsets inside a block (TOK: inside a token's page)
+  unsigned goff[kParts];      // per-lane source offsets inside a block (TOK: inside a token's page)
   unsigned ring;              // LDS address of this slot in stage 0
   unsigned ids_lds;           // this wave's two page-id windows
   const int* ids;
-  int pb, pe, slot, n_steps, num_pages, L, lane4;
+  int pb, pe, slot, n_steps, num_pages, L, lane_ids;
   int rlog;                   // log2(cache page size / 16)
   Ids next_id;                // table entries of the next transfer (read from LDS)
 
-  // In LDS, the 16-byte chunk at position pos of key row k (page slot j) holds
-  // dim chunk pos ^ sw(k, j), sw(k, j) = (k ^ 12 (j & 1)) & 15: K row reads and
-  // V transposed reads are then free of bank conflicts.
+  // In part jj of a block, lane (r, c) = (lane / (D / 16), lane % (D / 16))
+  // moves 16 bytes of key row k = R jj + r. In LDS, the 16-byte chunk at
+  // position c of key row k (page slot parity j) holds dim chunk c ^ sw(k, j)
+  // (Dim::sw): K row reads and V transposed reads are then free of bank conflicts.
   __device__ void init(const MainParams& p, const Geo& geo, uint8_t* smem, int wave, int slot_, int lane,
                        const uint8_t* cache_, unsigned ring_stage0, int off_ids) {
     cache = cache_;
     bt_row = p.block_tables + (int64_t)geo.b * p.block_table_stride;
-    page_stride = (uint64_t)(TOK ? 1 : kPageSize) * p.num_kv_heads * kHeadDim;
+    page_stride = (uint64_t)(TOK ? 1 : kPageSize) * p.num_kv_heads * D;
     slot = slot_;
     pb = geo.pb;
     pe = geo.pe;
@@ -247,35 +283,35 @@ struct PageStream {
     num_pages = p.num_pages;
     L = geo.L;
     rlog = p.page_ratio_log2;
-    const int g = lane >> 4, n = lane & 15, jpar = slot & 1;
-    lane4 = 4 * g;
+    const int r = lane / Dm::kChunks, c = lane % Dm::kChunks, jpar = slot & 1;
+    lane_ids = r * kParts;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int k = 4 * jj + g;
-      goff[jj] = (unsigned)(((TOK ? 0 : k * p.num_kv_heads) + geo.hkv) * kHeadDim + 16 * (n ^ ((k ^ (12 * jpar)) & 15)));
+    for (int jj = 0; jj < kParts; ++jj) {
+      const int k = Dm::kRowsPerKiB * jj + r;
+      goff[jj] = (unsigned)(((TOK ? 0 : k * p.num_kv_heads) + geo.hkv) * D + 16 * (c ^ Dm::sw(k, jpar)));
     }
-    ring = ring_stage0 + slot * kPageBytes;
+    ring = ring_stage0 + slot * Dm::kPageBytes;
     ids_lds = lds_addr(smem + off_ids) + wave * (2 * 64 * 4);
     ids = (const int*)(smem + off_ids) + wave * (2 * 64);
     next_id = Ids{};
   }
   __device__ bool has(int t) const { return t < n_steps && pb + kPagesPerStep * t + slot < pe; }
-  __device__ int count(int t) const { return has(t) ? kDmaPerWave : 0; }
+  __device__ int count(int t) const { return has(t) ? kParts : 0; }
   // Pages here are 16-token blocks. A cache page of 16 R tokens (R = 2^rlog)
   // holds R of them back to back in NHD order, so 16-token block pidx is part
   // pidx mod R of cache page block_tables[pidx / R], at 16-token index
   // block_tables[pidx / R] R + pidx mod R.
   // Windows (two slots, w even / odd): with 16 R-token pages entry k of window
   // w is the table entry of step 64 w + k; with one-token pages, window w
-  // covers steps 4 w .. 4 w + 3 and entry 16 s + 4 g + jj holds token 4 jj + g
-  // of step 4 w + s (a lane's four entries are adjacent). Tokens past the
+  // covers steps 4 w .. 4 w + 3 and entry 16 s + kParts r + jj holds token
+  // R jj + r of step 4 w + s (a lane's entries are adjacent). Tokens past the
   // sequence end read the last token's entry, so no unused entry is read.
   __device__ void fetch_window(int win, int lane) {
     if constexpr (TOK) {
-      const int s = lane >> 4, gg = (lane >> 2) & 3, jj = lane & 3;
+      const int s = lane >> 4, r = (lane & 15) / kParts, jj = lane % kParts;
       int pidx = pb + kPagesPerStep * (4 * win + s) + slot;
       pidx = pidx < pe ? pidx : pb;
-      const int tok = min(kPageSize * pidx + 4 * jj + gg, L - 1);
+      const int tok = min(kPageSize * pidx + Dm::kRowsPerKiB * jj + r, L - 1);
       dma_4b(bt_row, (unsigned)(4 * tok), ids_lds + (win & 1) * 256);
     } else {
       int pidx = pb + kPagesPerStep * (64 * win + lane) + slot;
@@ -299,30 +335,30 @@ struct PageStream {
   }
   __device__ Ids read_id(int t) const {
     if constexpr (TOK)
-      return *(const i32x4*)(ids + ((t >> 2) & 1) * 64 + (t & 3) * 16 + lane4);
+      return *(const Ids*)(ids + ((t >> 2) & 1) * 64 + (t & 3) * 16 + lane_ids);
     else
       return ids[((t >> 6) & 1) * 64 + (t & 63)];
   }
   __device__ int first_id(int t) const {            // scalar load, before the windows land
     return ((const const_i32*)bt_row)[(has(t) ? pb + kPagesPerStep * t + slot : pb) >> rlog];
   }
-  // TOK: source of part jj (this lane's token 4 jj + g), its page clamped into the cache
-  __device__ const uint8_t* token_src(const i32x4& e, int jj) const {
-    const int id = min(max(e[jj], 0), num_pages - 1);
+  // TOK: source of part jj (this lane's token R jj + r), its page clamped into the cache
+  __device__ const uint8_t* token_src(const Ids& e, int jj) const {
+    const int id = min(max((int)e[jj], 0), num_pages - 1);
     return cache + (uint64_t)id * page_stride + goff[jj];
   }
   __device__ void put(int t, const Ids& entry) {
-    const unsigned dst = ring + (t % kStages) * kStageBytes;
+    const unsigned dst = ring + (t % kStages) * Dm::kStageBytes;
     if constexpr (TOK) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) dma_1k_addr(token_src(entry, jj), dst + 1024 * jj);
+      for (int jj = 0; jj < kParts; ++jj) dma_1k_addr(token_src(entry, jj), dst + 1024 * jj);
     } else {
       const uint8_t* base = cache + (uint64_t)resolve(t, entry) * page_stride;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
+      for (int jj = 0; jj < kParts; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
     }
   }
-  // The transfer of step t in four parts that the caller spreads over its
+  // The transfer of step t in kParts parts that the caller spreads over its
   // work: begin() resolves the page (and refills the window when due),
   // part(q, jj) moves the jj-th KiB.
   struct Pending {
@@ -339,7 +375,7 @@ struct PageStream {
         q.e = next_id;
       else
         q.base = cache + (uint64_t)resolve(t, __builtin_amdgcn_readfirstlane(next_id)) * page_stride;
-      q.dst = ring + (t % kStages) * kStageBytes;
+      q.dst = ring + (t % kStages) * Dm::kStageBytes;
       next_id = read_id(t + 1);
     }
     return q;
@@ -354,27 +390,28 @@ struct PageStream {
   }
 };
 
-// Stores the staged 16-bit rows ([row][256] in LDS) of the work-group, all
-// 512 threads: fp16 o rows to the workspace with 16-byte streaming stores, or,
-// with a single segment, the final bf16 rows to out with 8-byte stores (out
-// rows are 8-byte aligned).
-template <int G>
+// Stores the staged 16-bit rows ([row][D] in LDS) of the work-group, all
+// 512 threads: fp16 o rows to the workspace (row stride kHeadDim) with 16-byte
+// streaming stores, or, with a single segment, the final bf16 rows to out with
+// 8-byte stores (out rows are 8-byte aligned).
+template <int G, int D>
 __device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
+  constexpr int kQuads = D / 4, kOcts = D / 8;   // 8-byte and 16-byte pieces of a row
   if (p.direct) {
-    for (int idx = threadIdx.x; idx < geo.rows * 64; idx += kThreads) {
-      const int row = idx >> 6, c = idx & 63;
+    for (int idx = threadIdx.x; idx < geo.rows * kQuads; idx += kThreads) {
+      const int row = idx / kQuads, c = idx % kQuads;
       const int i = row / G, gg = row - (row / G) * G;
       uint16_t* dst = p.out + (int64_t)(geo.q0 + i) * p.out_stride_token + (int64_t)(geo.h * G + gg) * p.out_stride_head + 4 * c;
-      *(uint2*)dst = *(const uint2*)(obuf + row * 512 + 8 * c);
+      *(uint2*)dst = *(const uint2*)(obuf + row * (2 * D) + 8 * c);
     }
     return;
   }
   const int T = p.total_q, Hq = p.num_q_heads;
-  for (int idx = threadIdx.x; idx < geo.rows * 32; idx += kThreads) {
-    const int row = idx >> 5, c = idx & 31;
+  for (int idx = threadIdx.x; idx < geo.rows * kOcts; idx += kThreads) {
+    const int row = idx / kOcts, c = idx % kOcts;
     const int i = row / G, gg = row - (row / G) * G;
     uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + geo.q0 + i) * Hq + geo.h * G + gg) * kHeadDim + 8 * c;
-    __builtin_nontemporal_store(*(const u32x4*)(obuf + row * 512 + 16 * c), (u32x4*)dst);
+    __builtin_nontemporal_store(*(const u32x4*)(obuf + row * (2 * D) + 16 * c), (u32x4*)dst);
   }
 }
 
@@ -393,9 +430,11 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // lazy softmax, P to LDS, row sums; writes m and l of the segment. With F8,
 // Q is quantised per row to e4m3 (scale amax / 448, folded into that row's
 // score multiplier), S^T runs on the fp8 MFMA and P is rounded to e4m3.
-template <int G, int NRB, int MODE, bool TOK>
+template <int G, int NRB, int MODE, bool TOK, int D>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
-  using C = Cfg<G>;
+  using C = Cfg<G, D>;
+  using Dm = Dim<D>;
+  constexpr int kPageBytes = Dm::kPageBytes, kStageBytes = Dm::kStageBytes, kKU = Dm::kKU;
   constexpr bool F8 = MODE == kModeFp8QP;    // e4m3 Q, S^T on the fp8 MFMA
   constexpr bool F8P = MODE != kMode16;      // e4m3 P
   const int tid = threadIdx.x;
@@ -412,24 +451,25 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   const bool capped = p.softcap > 0.f;
   uint8_t* const k_ring = smem + C::kOffStage;
 
-  PageStream<TOK> ks;   // K of page slot w: streamed by P.V wave w + 4, read here
+  PageStream<TOK, D> ks;   // K of page slot w: streamed by P.V wave w + 4, read here
   ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
 
   // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
   // phase 1) by page-style transfers, 16-byte chunk c of row r at position
   // c ^ (r & 15), score wave w moving rows 16w..16w+15, while the P.V waves
   // start the K and V streams. Q moves to registers after the first barrier.
+  constexpr int kQRow = Dm::kQRowBytes, kQRpk = Dm::kQRowsPerKiB, kQLanes = 64 / kQRpk;
   uint8_t* const q_stage = smem + C::kOffStage + (kStages + 2) * kStageBytes;
   if (n_steps > 0) {
     if (w < NRB) {
       const uint8_t* q_base = (const uint8_t*)(p.q + (int64_t)q0 * p.q_stride_token + (int64_t)h * G * p.q_stride_head);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 16 * w + 2 * k + (lane >> 5);
+      for (int k = 0; k < 16 / kQRpk; ++k) {
+        const int r = 16 * w + kQRpk * k + lane / kQLanes;
         const int rr = r < rows ? r : 0;            // padding rows read row 0, zeroed in registers
         const int i = rr / G, gg = rr - (rr / G) * G;
-        const unsigned voff = (unsigned)((i * p.q_stride_token + gg * p.q_stride_head) * 2) + 16u * ((lane & 31) ^ (r & 15));
-        dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + 2 * k) * 512);
+        const unsigned voff = (unsigned)((i * p.q_stride_token + gg * p.q_stride_head) * 2) + 16u * ((lane % kQLanes) ^ (r & 15));
+        dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + kQRpk * k) * kQRow);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -438,8 +478,9 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
   // With F8 (q8): byte b of k-step ks holds dim 128 ks + 32 g + b, and c2r is
   // the row's score multiplier c2 * amax / 448.
-  bf16x8 qop[F8 ? 1 : NRB][4][2];
-  i32x8 q8[F8 ? NRB : 1][2];
+  constexpr int kKS8 = D / 128;   // k-steps of the fp8 score MFMA
+  bf16x8 qop[F8 ? 1 : NRB][kKU][2];
+  i32x8 q8[F8 ? NRB : 1][kKS8];
   float c2r[NRB], inv_c2r[NRB];
   float cap_a[NRB], cap_b[NRB];   // soft-cap in raw-score units: s -> cap_b tanh(cap_a s)
   auto load_q = [&]() {
@@ -448,14 +489,14 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       for (int rb = 0; rb < NRB; ++rb) {
         const int r = 16 * rb + n;
         const bool pad = r >= rows;
-        bf16x8 x[2][4];
+        bf16x8 x[kKS8][4];
         float amax = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < kKS8; ++ks)
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
             const int pos = (16 * ks + 4 * g + c4) ^ n;
-            const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
+            const bf16x8 v = *(const bf16x8*)(q_stage + r * kQRow + 16 * pos);
             x[ks][c4] = pad ? bf16x8{} : v;
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[ks][c4][e]));
@@ -466,7 +507,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         c2r[rb] = c2 / qs;
         inv_c2r[rb] = 1.0f / c2r[rb];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < kKS8; ++ks)
 #pragma unroll
           for (int d = 0; d < 8; ++d) {
             const bf16x8& xv = x[ks][d >> 1];
@@ -485,25 +526,25 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       const int r = 16 * rb + n;
       const bool pad = r >= rows;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kKU; ++u)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int pos = (8 * u + 2 * g + hh) ^ n;
-          const bf16x8 v = *(const bf16x8*)(q_stage + r * 512 + 16 * pos);
+          const bf16x8 v = *(const bf16x8*)(q_stage + r * kQRow + 16 * pos);
           qop[rb][u][hh] = pad ? bf16x8{} : v;
         }
     }
   };
 
   // ---- per-lane LDS addresses
-  // K of key n: bf16 path chunks 4u + g (u = 0..3); fp8 path chunks 2g, 2g+1
-  // (k-step 0) and 8 + 2g, 9 + 2g (k-step 1); a chunk c sits at c ^ sw
-  const unsigned ksw = (unsigned)((n ^ (12 * (w & 1))) & 15);
-  unsigned k_off[4];
+  // K of key n: bf16 path chunks 4u + g (u < D / 64); fp8 path chunks 2g, 2g+1
+  // of k-step u / 2 (8 chunks per k-step); a chunk c sits at c ^ sw
+  const unsigned ksw = (unsigned)Dm::sw(n, w & 1);
+  unsigned k_off[kKU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kKU; ++u) {
     const unsigned c = F8 ? (unsigned)(2 * g + (u & 1) + 8 * (u >> 1)) : (unsigned)(4 * u + g);
-    k_off[u] = C::kOffStage + w * kPageBytes + 256 * n + 16u * (c ^ ksw);
+    k_off[u] = C::kOffStage + w * kPageBytes + D * n + 16u * (c ^ ksw);
   }
   // P of row 16 rb + n, keys 4g..4g+3 of slot w: half (w & 1) of the 16-byte
   // A operand of lane (g, n) in k-step w >> 1
@@ -529,7 +570,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   // from LDS by the caller). In tail steps the page may be missing and keys
   // past a row's causal limit (or the sequence end) are masked to -inf;
   // steady-state steps need neither.
-  auto score_step = [&](int t, const u32x4 (&kraw)[4], auto tail) {
+  auto score_step = [&](int t, const u32x4 (&kraw)[kKU], auto tail) {
     constexpr bool kTail = decltype(tail)::value;
     const int pidx = pb + kPagesPerStep * t + w;
     if (!kTail || ks.has(t)) {
@@ -537,14 +578,14 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       for (int rb = 0; rb < NRB; ++rb) sv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (F8) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < kKS8; ++ks) {
           const i32x8 ka = cat8(kraw[2 * ks], kraw[2 * ks + 1]);
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) sv[rb] = mfma_fp8_16x16x128(ka, q8[rb][ks], sv[rb]);
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kKU; ++u) {
           const bf16x8 k0 = fp8x8_to_bf16(kraw[u][0], kraw[u][1]);
           const bf16x8 k1 = fp8x8_to_bf16(kraw[u][2], kraw[u][3]);
 #pragma unroll
@@ -658,10 +699,10 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     const bool have_s = !kTail || t < n_steps;
     unsigned flag_word = 0;
     if (have_p) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((kst + 3) & 1));
-    u32x4 kraw[4];
+    u32x4 kraw[kKU];
     if (!kTail || ks.has(t)) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kraw[u] = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
+      for (int u = 0; u < kKU; ++u) kraw[u] = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
     }
     if (have_p) form_p(t - 1, (kst + 3) & 1, flag_word);
     if (have_s) {
@@ -755,16 +796,20 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
   }
   lds_barrier();   // o staged
-  store_rows<G>(p, geo, smem + C::kOffObuf);
+  store_rows<G, D>(p, geo, smem + C::kOffObuf);
 }
 
 // P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
 // NRB row blocks; stages its slice of the segment's normalised output o. With
 // F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
 // e4m3 bytes.
-template <int G, int NRB, int MODE, bool TOK>
+template <int G, int NRB, int MODE, bool TOK, int D>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
-  using C = Cfg<G>;
+  using C = Cfg<G, D>;
+  using Dm = Dim<D>;
+  constexpr int kPageBytes = Dm::kPageBytes, kStageBytes = Dm::kStageBytes, kVDims = Dm::kVDims;
+  constexpr int kParts = Dm::kDmaPerWave;   // 1 KiB parts per stream and step
+  constexpr int NDB = kVDims / 16;          // 16-dim output blocks of this wave
   constexpr bool F8 = MODE != kMode16;       // e4m3 P and V on the fp8 MFMA
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -778,7 +823,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   // Both blocks of page slot v stream through this wave: K (page-id windows
   // in the slot of score wave v, which streams nothing) three steps ahead of
   // its use by the score waves, V three steps ahead of its use here.
-  PageStream<TOK> ks, vs;
+  PageStream<TOK, D> ks, vs;
   ks.init(p, geo, smem, v, v, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
   vs.init(p, geo, smem, w, v, lane, p.v_cache, lds_addr(v_ring), C::kOffIds);
   if (n_steps > 0) {
@@ -792,7 +837,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         vs.fetch_window(1, lane);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      const i32x4 id0 = ks.read_id(0), id1 = ks.read_id(1), id2 = ks.read_id(2);
+      const auto id0 = ks.read_id(0), id1 = ks.read_id(1), id2 = ks.read_id(2);
       if (ks.has(0)) ks.put(0, id0);
       if (ks.has(1)) ks.put(1, id1);
       if (ks.has(2)) ks.put(2, id2);
@@ -815,11 +860,11 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   // of group g; ds_read_b64_tr_b8 hands lane n byte k of source lane 2k + n/8.
   const int vpar = (n >> 3) & 1;
   const int vkey = 4 * g + ((n >> 1) & 3);
-  const unsigned vsw = 16u * ((vkey ^ (12 * vpar)) & 15);
-  unsigned v_off[4];
+  const unsigned vsw = 16u * (unsigned)Dm::sw(vkey, vpar);
+  unsigned v_off[NDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-    v_off[db] = C::kOffStage + kStages * kStageBytes + vpar * kPageBytes + 256 * vkey + 8 * (n & 1) +
+  for (int db = 0; db < NDB; ++db)
+    v_off[db] = C::kOffStage + kStages * kStageBytes + vpar * kPageBytes + D * vkey + 8 * (n & 1) +
                 ((unsigned)(kVDims * v + 16 * db) ^ vsw);
   const int p_off = C::kOffP + lane * 16;
   const float* const alpha_buf = (const float*)(smem + C::kOffAlpha);
@@ -830,18 +875,19 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   // ds_read_b64_tr_b8 of 8 keys each: in its 16-lane group, source lane
   // 2k + hb supplies the 8 dims at +8 hb of key 32 q + 8 j + k.
   constexpr int NRT = (NRB + 1) / 2;    // 32-row tiles
-  unsigned v8_off[F8 ? 2 : 1][4];
+  constexpr int NDT = kVDims / 32;      // 32-dim tiles of this wave
+  unsigned v8_off[F8 ? NDT : 1][4];
   int p8_rd[F8 ? NRT : 1];
   if constexpr (F8) {
     const int q = lane >> 5, sub = (lane >> 4) & 1, src = lane & 15, kk8 = src >> 1, hb = src & 1;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int slot = 2 * q + (j >> 1), kin = 8 * (j & 1) + kk8;
-        const unsigned chunk = (unsigned)(4 * v + 2 * dt + sub);
-        const unsigned sw = (unsigned)((kin ^ (12 * (slot & 1))) & 15);
-        v8_off[dt][j] = C::kOffStage + kStages * kStageBytes + slot * kPageBytes + 256 * kin + 16u * (chunk ^ sw) + 8 * hb;
+        const unsigned chunk = (unsigned)((kVDims / 16) * v + 2 * dt + sub);
+        const unsigned sw = (unsigned)Dm::sw(kin, slot & 1);
+        v8_off[dt][j] = C::kOffStage + kStages * kStageBytes + slot * kPageBytes + D * kin + 16u * (chunk ^ sw) + 8 * hb;
       }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -850,18 +896,18 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     }
   }
 
-  f32x4 acc[F8 ? 1 : NRB][4];
-  f32x16 acc8[F8 ? NRT : 1][2];
+  f32x4 acc[F8 ? 1 : NRB][NDB];
+  f32x16 acc8[F8 ? NRT : 1][F8 ? NDT : 1];
   if constexpr (F8) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) acc8[rt][dt] = f32x16{};
+      for (int dt = 0; dt < NDT; ++dt) acc8[rt][dt] = f32x16{};
   } else {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   bool slow1 = false;   // flag of step t-1 in phase t
@@ -879,30 +925,31 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     const int u = t - 2;
     const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
     const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
-    // K of step t+3 and V of step t+1: eight 1 KiB parts, spread over the
-    // MFMA groups below so that a part that waits for room in the memory
+    // K of step t+3 and V of step t+1: 2 kParts 1 KiB parts, spread over
+    // the MFMA groups below so that a part that waits for room in the memory
     // pipeline does not hold up the whole phase's arithmetic
-    const typename PageStream<TOK>::Pending kq = ks.begin(t + 3, lane);
-    const typename PageStream<TOK>::Pending vq = vs.begin(t + 1, lane);
+    constexpr int kAll = 2 * kParts;
+    const typename PageStream<TOK, D>::Pending kq = ks.begin(t + 3, lane);
+    const typename PageStream<TOK, D>::Pending vq = vs.begin(t + 1, lane);
     auto parts = [&](int d0, int d1) {
       __builtin_amdgcn_sched_barrier(0);
       for (int d = d0; d < d1; ++d) {
-        if (d < 4)
+        if (d < kParts)
           ks.part(kq, d);
         else
-          vs.part(vq, d - 4);
+          vs.part(vq, d - kParts);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     unsigned flag_word = 0;
     if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
     // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
-    i32x2 vraw[2][4];
+    i32x2 vraw[2][NDB > 4 ? NDB : 4];
     f16x8 pa[F8 ? 1 : NRB][2];
     i32x8 pa8[F8 ? NRT : 1];
     if (F8 && have_pv) {
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           vraw[dt][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + v8_off[dt][j] + vst * kStageBytes));
@@ -916,7 +963,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < NDB; ++db)
           vraw[kk][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (lds_i32x2*)(smem + v_off[db] + vst * kStageBytes + kk * 2 * kPageBytes));
 #pragma unroll
@@ -944,7 +991,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
               if (k < 4) lo |= m8 << (8 * k); else hi |= m8 << (8 * (k - 4));
             }
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
+            for (int dt = 0; dt < NDT; ++dt) {
               vraw[dt][j][0] &= (int)lo;
               vraw[dt][j][1] &= (int)hi;
             }
@@ -959,30 +1006,30 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           for (int c = 0; c < 4; ++c) {
             const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 32 * rt + 8 * c + 4 * (lane >> 5));
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
               for (int e = 0; e < 4; ++e) acc8[rt][dt][4 * c + e] *= a[e];
           }
       }
-      i32x8 vb[2];
+      i32x8 vb[NDT];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
         vb[dt] = i32x8{vraw[dt][0][0], vraw[dt][0][1], vraw[dt][1][0], vraw[dt][1][1],
                        vraw[dt][2][0], vraw[dt][2][1], vraw[dt][3][0], vraw[dt][3][1]};
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
           acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
-          const int gi = rt * 2 + dt;
-          parts(8 * gi / (2 * NRT), 8 * (gi + 1) / (2 * NRT));
+          const int gi = rt * NDT + dt;
+          parts(kAll * gi / (NDT * NRT), kAll * (gi + 1) / (NDT * NRT));
         }
     } else if (!F8 && have_pv) {
-      f16x8 vf[2][4];
+      f16x8 vf[2][NDB];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[kk][db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
+        for (int db = 0; db < NDB; ++db) vf[kk][db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
       if constexpr (kTail) {
         // keys of pages past the segment (never loaded: stale or uninitialised
         // LDS) and past the sequence end get V = 0, so P = 0 never meets a NaN
@@ -995,7 +1042,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
               const int key = kPageSize * page + 4 * g + (e & 3);
               const bool keep = page < pe && key < L;
 #pragma unroll
-              for (int db = 0; db < 4; ++db) vf[kk][db][e] = keep ? vf[kk][db][e] : (_Float16)0.f;
+              for (int db = 0; db < NDB; ++db) vf[kk][db][e] = keep ? vf[kk][db][e] : (_Float16)0.f;
             }
         }
       }
@@ -1004,7 +1051,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         for (int rb = 0; rb < NRB; ++rb) {
           const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 16 * rb + 4 * g);
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[rb][db][r] *= a[r];
         }
@@ -1014,20 +1061,20 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < NDB; ++db)
             acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
           const int gi = kk * NRB + rb;
-          parts(8 * gi / (2 * NRB), 8 * (gi + 1) / (2 * NRB));
+          parts(kAll * gi / (2 * NRB), kAll * (gi + 1) / (2 * NRB));
         }
     } else {
-      parts(0, 8);
+      parts(0, kAll);
     }
     // K of step t+1 and V of step t-1 (issued in phase t-2) must have landed;
     // the transfers of phases t-1 and t may fly
     if constexpr (kTail)
       wait_vm(ks.count(t + 2) + vs.count(t) + ks.count(t + 3) + vs.count(t + 1));
     else
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      wait_vm(4 * kParts);
     lds_barrier();
   };
 
@@ -1046,7 +1093,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
 
   lds_barrier();   // the score waves' row sums of every page slot
   const float* const lsum = (const float*)smem;
-  _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][256]
+  _Float16* const obuf = (_Float16*)(smem + C::kOffObuf);   // [row][D]
   uint16_t* const obuf_bits = (uint16_t*)obuf;
   const float vd = p.direct ? *(const const_f32*)p.v_descale : 1.f;
   if constexpr (F8) {
@@ -1062,8 +1109,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
           const float inv = l > 0.f ? vd / l : 0.f;
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const int at = row * kHeadDim + kVDims * v + 32 * dt + (lane & 31);
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int at = row * D + kVDims * v + 32 * dt + (lane & 31);
             if (p.direct)
               obuf_bits[at] = (uint16_t)bf16_rne(acc8[rt][dt][r] * inv);
             else
@@ -1085,8 +1132,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         // o = acc / l (0 with no visible key); a single segment writes out = vd o
         const float inv = l > 0.f ? vd / l : 0.f;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int at = row * kHeadDim + kVDims * v + 16 * db + n;
+        for (int db = 0; db < NDB; ++db) {
+          const int at = row * D + kVDims * v + 16 * db + n;
           if (p.direct)
             obuf_bits[at] = (uint16_t)bf16_rne(acc[rb][db][r] * inv);
           else
@@ -1096,22 +1143,22 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     }
   }
   lds_barrier();
-  store_rows<G>(p, geo, smem + C::kOffObuf);
+  store_rows<G, D>(p, geo, smem + C::kOffObuf);
 }
 
-template <int G, int NRB, int MODE, bool TOK>
+template <int G, int NRB, int MODE, bool TOK, int D>
 __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
   if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB, MODE, TOK>(p, geo, smem);
+    score_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
   else
-    pv_wave<G, NRB, MODE, TOK>(p, geo, smem);
+    pv_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
 }
 
-// TOK: the cache has one-token pages
-template <int G, int MODE, bool TOK>
+// TOK: the cache has one-token pages; D: head dim
+template <int G, int MODE, bool TOK, int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
-  using C = Cfg<G>;
+  using C = Cfg<G, D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
 
   const const_i32* cu = (const const_i32*)p.cu_seqlens_q;
@@ -1151,36 +1198,36 @@ splitkv_main_kernel(MainParams p) {
   const int nrb = (geo.rows + 15) >> 4;
   if constexpr (G == 16) {
     switch (nrb) {
-      case 1: verify_segment<16, 1, MODE, TOK>(p, geo, smem); break;
-      case 2: verify_segment<16, 2, MODE, TOK>(p, geo, smem); break;
-      case 3: verify_segment<16, 3, MODE, TOK>(p, geo, smem); break;
-      default: verify_segment<16, 4, MODE, TOK>(p, geo, smem); break;
+      case 1: verify_segment<16, 1, MODE, TOK, D>(p, geo, smem); break;
+      case 2: verify_segment<16, 2, MODE, TOK, D>(p, geo, smem); break;
+      case 3: verify_segment<16, 3, MODE, TOK, D>(p, geo, smem); break;
+      default: verify_segment<16, 4, MODE, TOK, D>(p, geo, smem); break;
     }
   } else if constexpr (G == 8) {
     switch (nrb) {
-      case 1: verify_segment<8, 1, MODE, TOK>(p, geo, smem); break;
-      case 2: verify_segment<8, 2, MODE, TOK>(p, geo, smem); break;
-      case 3: verify_segment<8, 3, MODE, TOK>(p, geo, smem); break;
-      default: verify_segment<8, 4, MODE, TOK>(p, geo, smem); break;
+      case 1: verify_segment<8, 1, MODE, TOK, D>(p, geo, smem); break;
+      case 2: verify_segment<8, 2, MODE, TOK, D>(p, geo, smem); break;
+      case 3: verify_segment<8, 3, MODE, TOK, D>(p, geo, smem); break;
+      default: verify_segment<8, 4, MODE, TOK, D>(p, geo, smem); break;
     }
   } else {
     if (nrb == 1)
-      verify_segment<4, 1, MODE, TOK>(p, geo, smem);
+      verify_segment<4, 1, MODE, TOK, D>(p, geo, smem);
     else
-      verify_segment<4, 2, MODE, TOK>(p, geo, smem);
+      verify_segment<4, 2, MODE, TOK, D>(p, geo, smem);
   }
 }
 
-// TOK: one-token cache pages
-template <int MODE, bool TOK>
-hipError_t launch_tok(const MainParams& p, int group, hipStream_t stream) {
+// TOK: one-token cache pages; D: head dim
+template <int MODE, bool TOK, int D>
+hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
   const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
   if (group == 16)
-    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
   else if (group == 8)
-    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
   else if (group == 4)
-    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1188,9 +1235,9 @@ hipError_t launch_tok(const MainParams& p, int group, hipStream_t stream) {
 
 // group: query heads per work-group (16, 8 or 4; 32 query heads per KV head run
 // as two 16-head work-groups, p.kv_split = 2)
-template <int MODE>
-hipError_t launch_mode(const MainParams& p, int group, hipStream_t stream) {
-  return p.token_pages ? launch_tok<MODE, true>(p, group, stream) : launch_tok<MODE, false>(p, group, stream);
+template <int MODE, int D>
+hipError_t launch_dim(const MainParams& p, int group, hipStream_t stream) {
+  return p.token_pages ? launch_shape<MODE, true, D>(p, group, stream) : launch_shape<MODE, false, D>(p, group, stream);
 }
 
 }  // namespace

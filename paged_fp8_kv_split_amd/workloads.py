@@ -97,6 +97,9 @@ WORKLOADS = {
     "prod": _uniform("prod", 16, 35000, 4, 16, 1, 16, seed=2, replicas=16),
     # the production shape over one-token pages (every key row at a random slot)
     "prod_page1": _uniform("prod_page1", 16, 35000, 4, 16, 1, 16, seed=2, replicas=16, page_size=1),
+    # the production shape at head_dim 128 (softmax scale 1 / sqrt(128))
+    "prod_hd128": _uniform("prod_hd128", 16, 35000, 4, 16, 1, 16, seed=6, replicas=16, head_dim=128,
+                           softmax_scale=1.0 / math.sqrt(128.0)),
     # GQA 8
     "gqa8": _uniform("gqa8", 16, 35000, 4, 8, 1, 16, seed=3, replicas=16),
     # long context and occupancy pair

@@ -103,7 +103,9 @@ CASES = [
     ("q rows just under 4 GiB", dict(q_stride_token=((1 << 31) // 3 - 4096) // 8 * 8), "gfx950", 0),
     ("out stride", dict(out_stride_head=2), "gfx950", INVALID),
     ("workspace misaligned", dict(workspace=0x180004), "gfx950", INVALID),
-    ("head_dim 128", dict(head_dim=128), "gfx950", UNSUPPORTED),
+    ("head_dim 128", dict(head_dim=128), "gfx950", OK),
+    ("head_dim 64", dict(head_dim=64), "gfx950", UNSUPPORTED),
+    ("head_dim 192", dict(head_dim=192), "gfx950", UNSUPPORTED),
     ("page 32", dict(page_size=32), "gfx950", OK),
     ("page 64", dict(page_size=64), "gfx950", OK),
     ("page 1", dict(page_size=1), "gfx950", OK),
