@@ -18,6 +18,11 @@ visible scores (aiter PR #7375 "gfx1250 fp8 varlen FMHA", Summary). Split-KV
 segmentation is an exact rewrite of these quantities, so the oracle does not
 depend on the segment count.
 
+The second workload, fp8 varlen prefill attention (aiter PR #7375, Summary:
+e4m3 Q/K/V with per-tensor descales, packed THD layout, qk head dim 192 and v
+head dim 128, causal aligned to the bottom right or not, optional LSE), is in
+``prefill.py``.
+
 Every function here is pinned by ``tests/test_oracle.py`` to something other
 than itself (a library routine, brute force, closed forms, invariants, and the
 value printed for the fp8 probability-underflow example on aiter PR #7375).
@@ -34,3 +39,4 @@ from .attention import (  # noqa: F401
     segment_partials,
     visible_key_count,
 )
+from .prefill import causal_visible, default_scale, kv_head_of, prefill_attend, prefill_lse  # noqa: F401
