@@ -4,6 +4,9 @@ The compute path is the HIP library ``libpfkv.so`` built from ``csrc/``; the
 Python side only marshals arguments to its C ABI (see ``binding.py``). The
 library is loaded on first use and a missing build raises ``RuntimeError``:
 there is no CPU fallback.
+
+A second workload, fp8 varlen prefill attention (``prefill_attn``), runs on the
+same library.
 """
 
 from .binding import (  # noqa: F401
@@ -11,6 +14,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     num_segments,
+    prefill_attn,
     set_debug,
     stream_read,
     verify_attn,

@@ -34,6 +34,41 @@ class PfkvError(RuntimeError):
         self.status = status
 
 
+class PfkvPrefillArgs(ctypes.Structure):
+    """Mirror of ``pfkv_prefill_args`` in include/pfkv_prefill.h (same field order and types)."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("q_descale", ctypes.c_void_p),
+        ("k_descale", ctypes.c_void_p),
+        ("v_descale", ctypes.c_void_p),
+        ("q_stride_token", ctypes.c_int64),
+        ("q_stride_head", ctypes.c_int64),
+        ("k_stride_token", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+        ("out_stride_token", ctypes.c_int64),
+        ("out_stride_head", ctypes.c_int64),
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+    ]
+
+
 class PfkvArgs(ctypes.Structure):
     """Mirror of ``pfkv_args`` in include/pfkv.h (same field order and types)."""
 
@@ -107,6 +142,10 @@ def load_library():
     lib.pfkv_stream_read.restype = ctypes.c_int
     lib.pfkv_set_debug.argtypes = [ctypes.c_int]
     lib.pfkv_set_debug.restype = ctypes.c_int
+    lib.pfkv_prefill_check_args.argtypes = [ctypes.POINTER(PfkvPrefillArgs), ctypes.c_char_p, ctypes.c_int]
+    lib.pfkv_prefill_check_args.restype = ctypes.c_int
+    lib.pfkv_prefill_fwd.argtypes = [ctypes.POINTER(PfkvPrefillArgs), ctypes.c_void_p]
+    lib.pfkv_prefill_fwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -307,3 +346,85 @@ def stream_read(buf: torch.Tensor, variant: int, page_order: Optional[torch.Tens
                                    int(variant), ctypes.c_void_p(_ptr(page_order) or 0), n_pages,
                                    ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(handle)))
     return sink
+
+
+# ---------------------------------------------------------------- prefill
+def build_prefill_args(q, k, v, q_descale, k_descale, v_descale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                       softmax_scale, causal, out, lse=None) -> PfkvPrefillArgs:
+    """Fill a ``pfkv_prefill_args`` from torch tensors (shapes and dtypes checked here)."""
+    q, k, v = _as_bytes(q), _as_bytes(k), _as_bytes(v)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise TypeError(f"{name} must be [tokens, heads, dim] with unit last stride")
+    if k.shape[:2] != v.shape[:2] or q.shape[2] != k.shape[2]:
+        raise TypeError("k / v must share [total_k, Hkv] and q / k their head dim")
+    if out.dtype != torch.bfloat16 or out.dim() != 3 or out.stride(2) != 1 or \
+            tuple(out.shape) != (q.shape[0], q.shape[1], v.shape[2]):
+        raise TypeError("out must be bf16 [total_q, Hq, Dv] with unit last stride")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 vector")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise TypeError("cu_seqlens_q / cu_seqlens_k must both hold num_seqs + 1 entries")
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != 1:
+            raise TypeError(f"{name} must be a one-element float32 tensor")
+    for name, t in (("k", k), ("v", v), ("out", out), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k), ("q_descale", q_descale), ("k_descale", k_descale),
+                    ("v_descale", v_descale)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
+            raise TypeError("lse must be a contiguous float32 [Hq, total_q] tensor")
+        if lse.device != q.device:
+            raise ValueError(f"lse must be on q's device ({q.device}), got {lse.device}")
+    a = PfkvPrefillArgs()
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.cu_seqlens_q, a.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    a.q_descale, a.k_descale, a.v_descale = q_descale.data_ptr(), k_descale.data_ptr(), v_descale.data_ptr()
+    a.q_stride_token, a.q_stride_head = q.stride(0), q.stride(1)
+    a.k_stride_token, a.k_stride_head = k.stride(0), k.stride(1)
+    a.v_stride_token, a.v_stride_head = v.stride(0), v.stride(1)
+    a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1)
+    a.num_seqs = cu_seqlens_q.numel() - 1
+    a.total_q, a.total_k = q.shape[0], k.shape[0]
+    a.num_q_heads, a.num_kv_heads = q.shape[1], k.shape[1]
+    a.head_dim_qk, a.head_dim_v = q.shape[2], v.shape[2]
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.softmax_scale = float(softmax_scale)
+    a.causal = 1 if causal else 0
+    return a
+
+
+def prefill_attn(q, k, v, q_descale, k_descale, v_descale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                 max_seqlen_k=None, softmax_scale=None, is_causal=False, return_lse=False, out=None, lse=None):
+    """fp8 varlen prefill attention; returns ``out`` (bf16 ``[total_q, Hq, 128]``),
+    or ``(out, lse)`` with ``return_lse`` (or an ``lse`` buffer given).
+
+    Same argument list as ``fmha_fwd_fp8_varlen_asm(q, k, v, q_descale, k_descale,
+    v_descale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+    softmax_scale=None, is_causal=False, return_lse=False, out=None)`` of aiter
+    PR #7375 (Changes). q / k / v: ``float8_e4m3fn`` (or uint8 codes) packed
+    ``[tokens, heads, dim]`` views with unit last stride (qk dim 192, v dim 128);
+    descales: one-element float32 tensors on q's device; softmax_scale defaults to
+    1 / sqrt(192). ``max_seqlen_k`` is accepted for the same signature and unused.
+    """
+    del max_seqlen_k
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(q.shape[2]) ** 0.5
+    a = build_prefill_args(q, k, v, q_descale, k_descale, v_descale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                           softmax_scale, is_causal, out, lse)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _raise_on(load_library().pfkv_prefill_fwd(ctypes.byref(a), ctypes.c_void_p(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def check_prefill_args(args: PfkvPrefillArgs, arch: str = "gfx950:sramecc+:xnack-", num_cus: int = 256) -> int:
+    """Host-only validation (no GPU): the library's status code for ``args``."""
+    return int(load_library().pfkv_prefill_check_args(ctypes.byref(args), arch.encode(), int(num_cus)))

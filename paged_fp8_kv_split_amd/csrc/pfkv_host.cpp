@@ -21,6 +21,7 @@
 
 #include "pfkv.h"
 #include "pfkv_internal.h"
+#include "pfkv_prefill.h"
 
 namespace {
 
@@ -431,6 +432,113 @@ int pfkv_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PFKV_LAUNCH, std::string("stream read: ") + hipGetErrorString(e));
+  }
+  return PFKV_OK;
+}
+
+// ---------------------------------------------------------------- prefill
+// The second workload (include/pfkv_prefill.h): fp8 varlen prefill attention
+// as aiter PR #7375 ("gfx1250 fp8 varlen FMHA") specifies it in its sections
+// Summary and Changes (e4m3 q/k/v with single-element fp32 descales on the
+// device, qk head dim 192 / v head dim 128, packed THD rows, optional lse
+// [Hq, total_q], causal aligned to the bottom right).
+
+int pfkv_prefill_check_args(const pfkv_prefill_args* a, const char* arch, int num_cus) {
+  g_last_error.clear();
+  if (a == nullptr) return fail(PFKV_INVALID, "args is NULL");
+  if (arch == nullptr) return fail(PFKV_INVALID, "arch is NULL");
+  if (num_cus <= 0) return fail(PFKV_INVALID, "num_cus must be positive");
+  const struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{a->q, "q"}, {a->k, "k"}, {a->v, "v"}, {a->out, "out"}, {a->cu_seqlens_q, "cu_seqlens_q"},
+              {a->cu_seqlens_k, "cu_seqlens_k"}, {a->q_descale, "q_descale"}, {a->k_descale, "k_descale"},
+              {a->v_descale, "v_descale"}};
+  for (const auto& x : ptrs)
+    if (x.p == nullptr) return fail(PFKV_INVALID, std::string(x.name) + " is NULL");
+  if (a->num_seqs < 1 || a->num_seqs > 65535) return fail(PFKV_INVALID, "num_seqs must be in [1, 65535]");
+  if (a->total_q < 1) return fail(PFKV_INVALID, "total_q must be >= 1");
+  if (a->total_k < 0) return fail(PFKV_INVALID, "total_k must be >= 0");
+  if (a->num_q_heads < 1 || a->num_q_heads > 65535 || a->num_kv_heads < 1)
+    return fail(PFKV_INVALID, "head counts must be positive (num_q_heads <= 65535)");
+  if (a->num_q_heads % a->num_kv_heads != 0) return fail(PFKV_INVALID, "num_q_heads % num_kv_heads != 0");
+  if (a->max_seqlen_q < 1 || a->max_seqlen_q > (1 << 30)) return fail(PFKV_INVALID, "max_seqlen_q must be in [1, 2^30]");
+  if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
+    return fail(PFKV_INVALID, "softmax_scale must be finite and positive");
+  const int64_t byte_strides[] = {a->q_stride_token, a->q_stride_head, a->k_stride_token,
+                                  a->k_stride_head,  a->v_stride_token, a->v_stride_head};
+  for (int64_t st : byte_strides)
+    if (st <= 0 || st % 16) return fail(PFKV_INVALID, "q / k / v strides must be positive multiples of 16 bytes");
+  if (a->out_stride_token <= 0 || a->out_stride_head <= 0 || a->out_stride_token % 4 || a->out_stride_head % 4)
+    return fail(PFKV_INVALID, "out strides must be positive multiples of 4 elements");
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16))
+    return fail(PFKV_INVALID, "q / k / v must be 16-byte aligned");
+  if (!aligned(a->out, 8)) return fail(PFKV_INVALID, "out must be 8-byte aligned");
+  if (!aligned(a->cu_seqlens_q, 4) || !aligned(a->cu_seqlens_k, 4) || !aligned(a->q_descale, 4) ||
+      !aligned(a->k_descale, 4) || !aligned(a->v_descale, 4) || !aligned(a->lse, 4))
+    return fail(PFKV_INVALID, "int32 / fp32 arguments must be 4-byte aligned");
+  if (!is_gfx950(arch)) return fail(PFKV_UNSUPPORTED, std::string("device is ") + arch + ", kernels are gfx950");
+  if (a->head_dim_qk != 192 || a->head_dim_v != 128)
+    return fail(PFKV_UNSUPPORTED, "head dims must be 192 (q, k) and 128 (v)");
+  return PFKV_OK;
+}
+
+int pfkv_prefill_fwd(const pfkv_prefill_args* a, void* stream) {
+  g_last_error.clear();
+  if (a == nullptr) return fail(PFKV_INVALID, "args is NULL");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  }
+  DeviceProps d;
+  int st = cached_props(device, &d);
+  if (st != PFKV_OK) return st;
+  st = pfkv_prefill_check_args(a, d.arch.c_str(), d.num_cus);
+  if (st != PFKV_OK) return st;
+  const struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{a->q, "q"}, {a->k, "k"}, {a->v, "v"}, {a->out, "out"}, {a->cu_seqlens_q, "cu_seqlens_q"},
+              {a->cu_seqlens_k, "cu_seqlens_k"}, {a->q_descale, "q_descale"}, {a->k_descale, "k_descale"},
+              {a->v_descale, "v_descale"}, {a->lse, "lse"}};
+  for (const auto& x : ptrs) {
+    if (x.p == nullptr) continue;   // only lse may be NULL here
+    st = check_device_pointer(x.p, device, x.name);
+    if (st != PFKV_OK) return st;
+  }
+  pfkv::PrefillParams p;
+  p.q = (const uint8_t*)a->q;
+  p.q_stride_token = a->q_stride_token;
+  p.q_stride_head = a->q_stride_head;
+  p.k = (const uint8_t*)a->k;
+  p.k_stride_token = a->k_stride_token;
+  p.k_stride_head = a->k_stride_head;
+  p.v = (const uint8_t*)a->v;
+  p.v_stride_token = a->v_stride_token;
+  p.v_stride_head = a->v_stride_head;
+  p.out = (uint16_t*)a->out;
+  p.out_stride_token = a->out_stride_token;
+  p.out_stride_head = a->out_stride_head;
+  p.lse = a->lse;
+  p.cu_seqlens_q = a->cu_seqlens_q;
+  p.cu_seqlens_k = a->cu_seqlens_k;
+  p.q_descale = a->q_descale;
+  p.k_descale = a->k_descale;
+  p.v_descale = a->v_descale;
+  p.num_seqs = a->num_seqs;
+  p.total_q = a->total_q;
+  p.total_k = a->total_k;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.max_seqlen_q = a->max_seqlen_q;
+  p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
+  p.causal = a->causal != 0 ? 1 : 0;
+  e = pfkv::launch_prefill(p, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PFKV_LAUNCH, std::string("prefill launch: ") + hipGetErrorString(e));
   }
   return PFKV_OK;
 }

@@ -79,6 +79,28 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// fp8 varlen prefill (the second workload): e4m3 Q/K/V rows in packed THD
+// layout, qk head dim 192, v head dim 128.
+struct PrefillParams {
+  const uint8_t* q;            // [total_q, Hq, 192] e4m3 bytes
+  int64_t q_stride_token, q_stride_head;   // bytes, multiples of 16
+  const uint8_t* k;            // [total_k, Hkv, 192]
+  int64_t k_stride_token, k_stride_head;
+  const uint8_t* v;            // [total_k, Hkv, 128]
+  int64_t v_stride_token, v_stride_head;
+  uint16_t* out;               // bf16 bits [total_q, Hq, 128]
+  int64_t out_stride_token, out_stride_head;   // elements, multiples of 4
+  float* lse;                  // optional [Hq][total_q]
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  int32_t num_seqs, total_q, total_k, num_q_heads, num_kv_heads, max_seqlen_q;
+  float scale_log2;            // softmax_scale * log2(e); times q and k descales on the device
+  int32_t causal;
+};
+
 // Debug-mode precondition check of the device-side inputs.
 struct CheckParams {
   const int32_t* cu_seqlens_q;
@@ -96,6 +118,7 @@ hipError_t launch_splitkv_main_fp8(const MainParams& p, int group, hipStream_t s
 hipError_t launch_splitkv_main_hd128(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_precondition_check(const CheckParams& p, int32_t* status, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,
                               int64_t num_pages, uint32_t* sink, hipStream_t stream);
 

@@ -1,0 +1,344 @@
+// fp8 varlen prefill attention (gfx950): e4m3 Q/K/V with per-tensor descales,
+// packed THD rows, qk head dim 192, v head dim 128, bf16 output, optional LSE,
+// causal aligned to the bottom right or not. What it computes follows aiter PR
+// #7375 ("gfx1250 fp8 varlen FMHA"), section Summary; the kernel there is
+// gfx1250 assembly, this one is written for gfx950:
+//
+// * A work-group of 8 waves serves 256 query rows of one (sequence, query
+//   head); wave w owns rows 32 w .. 32 w + 31 whole (no cross-wave softmax).
+// * Key tiles of 64 rows stream HBM/L2 -> LDS through a 3-stage ring with
+//   global_load_lds_dwordx4 (one barrier per tile, two tiles in flight). K rows
+//   (192 bytes) sit at rotated 16-byte positions and V rows (128 bytes) at
+//   XOR-swizzled ones, so the MFMA operand reads below are free of bank
+//   conflicts.
+// * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (three k-steps over the
+//   192 dims), Q held in registers. A lane then holds 32 scores of one query row.
+// * Online softmax in the log2 domain with a lazy reference max (moved only
+//   when a row's max passes it by more than 8), so rescaling is rare.
+// * P in e4m3 with an E8M0 block scale per 32 keys of a row: each block's
+//   probabilities are scaled by a power of two that puts their maximum in
+//   [128, 256) before rounding, and the scale rides in the MFMA's B-scale
+//   operand. Small probabilities then keep their 3-bit mantissa instead of
+//   flushing to zero (the underflow the same page's review works through).
+//   The row sum l adds the rounded, rescaled values, so O and the LSE use the
+//   same weights. On this MFMA the scale in lane c + 32 kb covers bytes
+//   16 kb .. 16 kb + 15 of both lane halves of column c (measured), which here
+//   are keys 32 kb .. 32 kb + 31 of the row: both lanes of a row share each
+//   block's exponent, and lane half kb supplies block kb's.
+// * O^T = V^T P^T on the same scaled MFMA (four 32-dim tiles), V^T from LDS by
+//   ds_read_b64_tr_b8, so each lane's accumulators belong to its own row.
+#include "pfkv_internal.h"
+
+namespace pfkv {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+typedef __attribute__((address_space(4))) const float const_f32;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kTileRows = kWaves * kRowsPerWave;      // 256 query rows per work-group
+constexpr int kKeys = 64;                             // keys per tile
+constexpr int kDqk = 192, kDv = 128;
+constexpr int kKBytes = kKeys * kDqk;                 // 12 KiB
+constexpr int kVBytes = kKeys * kDv;                  // 8 KiB
+constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kStages = 3;
+constexpr int kKParts = kKBytes / 1024;               // 12 transfers of 1 KiB
+constexpr int kParts = kKParts + kVBytes / 1024;      // 20 per tile
+constexpr float kLazySlack = 8.0f;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 1 KiB HBM -> LDS transfer, 16 bytes per lane from its own 64-bit address
+// to LDS address lds + 16 i. M0 carries the LDS base; it is saved and restored.
+__device__ __forceinline__ void dma_1k_addr(const uint8_t* addr, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(addr), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// K row `key` keeps its 16-byte chunk c at position (c + rot(key)) mod 12.
+__device__ __forceinline__ int k_rot(int key) { return (key >> 2) & 3; }
+// V row `key` keeps its 16-byte chunk c at position c ^ vsw(key).
+__device__ __forceinline__ int v_sw(int key) { return 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1); }
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c, int scale_a, int scale_b) {
+  // e4m3 A and B with E8M0 block scales (one per lane's 32 k-elements)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+  const int b = blockIdx.z, hq = blockIdx.y;
+  const int qt = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;   // long tiles first
+
+  // sequence geometry, clamped so that every access stays inside the buffers
+  const const_i32* cq = (const const_i32*)p.cu_seqlens_q;
+  const const_i32* ck = (const const_i32*)p.cu_seqlens_k;
+  const int q0 = min(max(cq[b], 0), p.total_q);
+  const int lq = min(max(cq[b + 1] - q0, 0), min(p.max_seqlen_q, p.total_q - q0));
+  const int k0 = min(max(ck[b], 0), p.total_k);
+  const int lk = min(max(ck[b + 1] - k0, 0), p.total_k - k0);
+  const int i0 = qt * kTileRows;
+  if (i0 >= lq) return;
+  const int hkv = hq / (p.num_q_heads / p.num_kv_heads);
+  const int rows_end = min(i0 + kTileRows, lq);
+  // keys some row of the work-group (the wave) can see
+  const int kv_end = CAUSAL ? min(max(lk - lq + rows_end, 0), lk) : lk;
+  const int n_tiles = (kv_end + kKeys - 1) / kKeys;
+  const int r0 = i0 + kRowsPerWave * w;              // this wave's first row
+  const bool wave_rows = r0 < lq;
+  const int kv_end_w = !wave_rows ? 0 : (CAUSAL ? min(max(lk - lq + min(r0 + kRowsPerWave, lq), 0), lk) : lk);
+  const int row = r0 + col;                          // this lane's query row
+  const bool row_ok = row < lq;
+
+  const float c2 = *(const const_f32*)p.q_descale * *(const const_f32*)p.k_descale * p.scale_log2;
+
+  // ---- Q^T operand: lane (col, h) holds dims 64 kc + 32 h .. + 31 of its row
+  i32x8 qop[3];
+  {
+    const uint8_t* qrow = p.q + (int64_t)(q0 + (row_ok ? row : 0)) * p.q_stride_token + (int64_t)hq * p.q_stride_head;
+#pragma unroll
+    for (int kc = 0; kc < 3; ++kc) {
+      const i32x4 lo = *(const i32x4*)(qrow + 64 * kc + 32 * h);
+      const i32x4 hi = *(const i32x4*)(qrow + 64 * kc + 32 * h + 16);
+      qop[kc] = row_ok ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]} : i32x8{};
+    }
+  }
+
+  // ---- tile transfers: wave w moves parts w, w + 8, w + 16 (< 20) of every tile
+  const uint8_t* kbase = p.k + (int64_t)k0 * p.k_stride_token + (int64_t)hkv * p.k_stride_head;
+  const uint8_t* vbase = p.v + (int64_t)k0 * p.v_stride_token + (int64_t)hkv * p.v_stride_head;
+  const unsigned ring = lds_addr(smem);
+  auto issue = [&](int t) {
+    const int kt = kKeys * t;
+    const unsigned stage = ring + (t % kStages) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int m = w + 8 * j;
+      if (m < kKParts) {
+        const int u = 64 * m + lane;                    // 16-byte unit of the K tile
+        const int key = u / 12, pos = u - 12 * key;
+        const int c = (pos + 12 - k_rot(key)) % 12;
+        const int kg = min(kt + key, lk - 1);           // keys past the end read the last (masked)
+        dma_1k_addr(kbase + (int64_t)kg * p.k_stride_token + 16 * c, stage + 1024 * m);
+      } else if (m < kParts) {
+        const int mm = m - kKParts;
+        const int key = 8 * mm + (lane >> 3), pos = lane & 7;
+        const int kg = min(kt + key, lk - 1);
+        dma_1k_addr(vbase + (int64_t)kg * p.v_stride_token + 16 * (pos ^ v_sw(key)), stage + kKBytes + 1024 * mm);
+      }
+    }
+  };
+  const bool three = w < kParts - 16;                 // waves 0-3 move three parts, 4-7 two
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+
+  // ---- per-lane LDS read offsets
+  // K operand (S^T = K Q^T): key 32 kb + col, chunks 4 kc + 2 h and + 1
+  // V^T operand (O^T = V^T P^T): source lane (gq, s = 2 k + hb) of instruction
+  // mm reads the 8 bytes at +8 hb of dim block 2 dt + gq of key
+  // 32 (mm >> 1) + 16 (mm & 1) + 8 (k >> 2) + 4 h + (k & 3); ds_read_b64_tr_b8
+  // hands lane n of the group byte k of source lane 2 k + n / 8, so lane
+  // (col, h) receives dim 32 dt + col of the keys of k-slots 32 h + 8 mm .. + 7.
+  int v_off[4][4];
+  {
+    const int gq = (lane >> 4) & 1, s = lane & 15, k = s >> 1, hb = s & 1;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int key = 32 * (mm >> 1) + 16 * (mm & 1) + 8 * (k >> 2) + 4 * h + (k & 3);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) v_off[mm][dt] = kKBytes + key * kDv + 16 * ((2 * dt + gq) ^ v_sw(key)) + 8 * hb;
+    }
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_ref = -__builtin_inff();     // reference max of this lane's row (log2 units)
+  float thr = -__builtin_inff();       // raw-score threshold (m_ref + slack) / c2
+  float l_lane = 0.f;                  // this lane's share of the row sum
+
+  for (int t = 0; t < n_tiles; ++t) {
+    // this wave's transfers of tile t have landed (tile t + 1 may fly), then
+    // everyone's have, and everyone is done with the stage tile t + 2 reuses
+    if (t + 1 < n_tiles) {
+      if (three)
+        asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();
+    if (t + 2 < n_tiles) issue(t + 2);
+    const int kt = kKeys * t;
+    if (kt >= kv_end_w) continue;                   // every key of the tile is masked for this wave
+    const uint8_t* stage = smem + (t % kStages) * kStageBytes;
+
+    // scores: s[kb][r] = S^T[key 32 kb + 8 (r >> 2) + 4 h + (r & 3)][row]
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x16{};
+      const int key = 32 * kb + col;
+      const int rot = k_rot(key);
+#pragma unroll
+      for (int kc = 0; kc < 3; ++kc) {
+        const int c = 4 * kc + 2 * h;
+        const i32x4 lo = *(const i32x4*)(stage + 16 * (12 * key + (c + rot) % 12));
+        const i32x4 hi = *(const i32x4*)(stage + 16 * (12 * key + (c + 1 + rot) % 12));
+        const i32x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sc[kb] = mfma8(ka, qop[kc], sc[kb], 127, 127);
+      }
+    }
+    // masks: keys past the sequence, and (causal) past the row's diagonal
+    const bool edge = kt + kKeys > lk || (CAUSAL && kt + kKeys - 1 > lk - lq + r0);
+    if (edge) {
+      const int lim = CAUSAL ? min(lk - 1, lk - lq + row) : lk - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          sc[kb][r] = key <= lim ? sc[kb][r] : -__builtin_inff();
+        }
+    }
+    // lazy reference max of the row (both lanes of the row agree)
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool move = mx > thr;
+    if (__any(move)) {
+      float alpha = 1.f;
+      if (move) {
+        const float m_new = mx * c2;
+        alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 when m_ref was -inf
+        m_ref = m_new;
+        thr = (m_new + kLazySlack) / c2;
+      }
+      l_lane *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    // P = 2^(s c2 - m) (0 for a masked key), then e4m3 with a power-of-two
+    // scale per block of 32 keys (block kb: this lane's bytes 16 kb .. + 15 and
+    // its partner lane's)
+    const float mref = m_ref == -__builtin_inff() ? 0.f : m_ref;
+    float pv[32];
+    float pm[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
+        pv[16 * kb + r] = edge && sc[kb][r] == -__builtin_inff() ? 0.f : x;
+        pm[kb] = fmaxf(pm[kb], pv[16 * kb + r]);
+      }
+    // block exponent e with pm 2^-e in [128, 256); E8M0 byte 127 + e. P never
+    // exceeds 2^8 (lazy max), so e <= 1; a block whose largest probability is
+    // below 2^-100 contributes nothing and is zeroed (e = 0), so e >= -107.
+    int eb[2];
+    float up[2], down[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float m = fmaxf(pm[kb], __shfl_xor(pm[kb], 32, 64));
+      const bool live = m >= 0x1p-100f;
+      eb[kb] = live ? (int)((__float_as_uint(m) >> 23) & 255) - 127 - 7 : 0;
+      up[kb] = live ? __uint_as_float((uint32_t)(127 - eb[kb]) << 23) : 0.f;   // 2^-e
+      down[kb] = __uint_as_float((uint32_t)(127 + eb[kb]) << 23);              // 2^e
+    }
+    int pw[8];
+    float lsum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = up[j >> 2];
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j] * f, pv[4 * j + 1] * f, 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2] * f, pv[4 * j + 3] * f, word, true);
+      pw[j] = word;
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const f32x2 bb = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      lsum[j >> 2] += (a[0] + a[1]) + (bb[0] + bb[1]);
+    }
+    l_lane += lsum[0] * down[0] + lsum[1] * down[1];
+    const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
+    const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    // O^T += V^T P^T over the tile's 64 keys, four 32-dim tiles
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      i32x2 vr[4];
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+        vr[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(stage + v_off[mm][dt]));
+      const i32x8 va = {vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]};
+      o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
+    }
+  }
+
+  // ---- epilogue: o = O / l (0 without a visible key), bf16 out, optional lse
+  if (!wave_rows) return;
+  const float l = l_lane + __shfl_xor(l_lane, 32, 64);
+  if (!row_ok) return;
+  const float inv = l > 0.f ? *(const const_f32*)p.v_descale / l : 0.f;
+  uint16_t* dst = p.out + (int64_t)(q0 + row) * p.out_stride_token + (int64_t)hq * p.out_stride_head;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d = 32 * dt + 8 * c + 4 * h;
+      const uint32_t lo = bf16_rne(o[dt][4 * c] * inv) | (bf16_rne(o[dt][4 * c + 1] * inv) << 16);
+      const uint32_t hi = bf16_rne(o[dt][4 * c + 2] * inv) | (bf16_rne(o[dt][4 * c + 3] * inv) << 16);
+      *(uint2*)(dst + d) = make_uint2(lo, hi);
+    }
+  if (p.lse != nullptr && h == 0)
+    p.lse[(int64_t)hq * p.total_q + q0 + row] =
+        l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -__builtin_inff();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.max_seqlen_q + kTileRows - 1) / kTileRows), (unsigned)p.num_q_heads,
+                  (unsigned)p.num_seqs);
+  if (p.causal)
+    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pfkv

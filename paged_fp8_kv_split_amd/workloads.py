@@ -231,3 +231,114 @@ def permute_pool(case: Case, seed: int) -> Case:
     return Case(case.q, case.k_cache[idx].contiguous(), case.v_cache[idx].contiguous(), tables,
                 case.seq_lens, case.cu_seqlens_q, case.k_descale, case.v_descale,
                 case.softmax_scale, int(new_of_old[case.poison_page]), case.workload)
+
+
+# ---------------------------------------------------------------- prefill
+# Synthetic inputs of the second workload (fp8 varlen prefill, aiter PR #7375,
+# Performance): bf16-distributed data quantized per tensor to e4m3 with scale
+# amax / 448, packed THD rows, qk head dim 192 and v head dim 128.
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    lens: tuple                  # ((Lq, Lk), ...) per sequence
+    num_q_heads: int
+    num_kv_heads: int
+    causal: bool
+    seed: int
+    head_dim_qk: int = 192
+    head_dim_v: int = 128
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(a for a, _ in self.lens))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(b for _, b in self.lens))
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(max(a for a, _ in self.lens), 1)
+
+    @property
+    def flops(self) -> int:
+        """Both products over the visible (query, key) pairs: 2 (Dqk + Dv) per pair and head."""
+        pairs = 0
+        for lq, lk in self.lens:
+            if self.causal:
+                pairs += sum(max(0, min(lk, lk - lq + i + 1)) for i in range(lq))
+            else:
+                pairs += lq * lk
+        return 2 * (self.head_dim_qk + self.head_dim_v) * pairs * self.num_q_heads
+
+
+PREFILL_WORKLOADS = {
+    # the pages' target shape: one sequence of 12288 queries over 14336 keys, 96 heads
+    "prefill_12k": PrefillWorkload("prefill_12k", ((12288, 14336),), 96, 96, False, seed=7),
+    "prefill_12k_causal": PrefillWorkload("prefill_12k_causal", ((12288, 14336),), 96, 96, True, seed=8),
+    # small varlen parity batch: GQA 4, ragged lengths, fewer keys than queries, empty KV
+    "prefill_small": PrefillWorkload("prefill_small", ((300, 300), (129, 517), (64, 40), (17, 0), (1, 77)), 8, 2,
+                                     True, seed=9),
+}
+
+
+def prefill_workload(name: str, **overrides) -> PrefillWorkload:
+    w = PREFILL_WORKLOADS[name]
+    return replace(w, **overrides) if overrides else w
+
+
+@dataclass
+class PrefillCase:
+    """Inputs of one prefill call (torch tensors; q/k/v are e4m3fn codes as uint8)."""
+
+    q: torch.Tensor              # [total_q, Hq, 192]
+    k: torch.Tensor              # [total_k, Hkv, 192]
+    v: torch.Tensor              # [total_k, Hkv, 128]
+    cu_seqlens_q: torch.Tensor   # int32 [B + 1]
+    cu_seqlens_k: torch.Tensor   # int32 [B + 1]
+    q_descale: torch.Tensor      # float32 [1]
+    k_descale: torch.Tensor
+    v_descale: torch.Tensor
+    max_seqlen_q: int
+    causal: bool
+    workload: PrefillWorkload = field(repr=False)
+
+    def to(self, device) -> "PrefillCase":
+        mv = lambda t: t.to(device)
+        return PrefillCase(mv(self.q), mv(self.k), mv(self.v), mv(self.cu_seqlens_q), mv(self.cu_seqlens_k),
+                           mv(self.q_descale), mv(self.k_descale), mv(self.v_descale), self.max_seqlen_q,
+                           self.causal, self.workload)
+
+    def host_arrays(self):
+        """numpy inputs in the oracle's argument names."""
+        return dict(q=self.q.cpu().numpy(), k=self.k.cpu().numpy(), v=self.v.cpu().numpy(),
+                    cu_seqlens_q=self.cu_seqlens_q.cpu().numpy(), cu_seqlens_k=self.cu_seqlens_k.cpu().numpy(),
+                    q_descale=float(self.q_descale.item()), k_descale=float(self.k_descale.item()),
+                    v_descale=float(self.v_descale.item()), softmax_scale=None, causal=self.causal)
+
+
+def make_prefill_case(w: PrefillWorkload, device="cpu") -> PrefillCase:
+    """Draw workload ``w`` (seeded) directly on ``device``."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+
+    def quantized(shape):
+        vals = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16).float()
+        scale = float(vals.abs().max().item()) / FP8_MAX
+        return _quantize(vals, scale), scale
+
+    q, qd = quantized((w.total_q, w.num_q_heads, w.head_dim_qk))
+    k, kd = quantized((w.total_k, w.num_kv_heads, w.head_dim_qk))
+    v, vd = quantized((w.total_k, w.num_kv_heads, w.head_dim_v))
+    cq = np.zeros(w.num_seqs + 1, dtype=np.int32)
+    ck = np.zeros(w.num_seqs + 1, dtype=np.int32)
+    cq[1:] = np.cumsum([a for a, _ in w.lens])
+    ck[1:] = np.cumsum([b for _, b in w.lens])
+    f32 = lambda x: torch.tensor([x], dtype=torch.float32, device=device)
+    return PrefillCase(q, k, v, torch.from_numpy(cq).to(device), torch.from_numpy(ck).to(device), f32(qd), f32(kd),
+                       f32(vd), w.max_seqlen_q, w.causal, w)

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI (no GPU needed): exports, validation, heuristics."""
 
 import ctypes
+import glob
 import os
 import subprocess
 import re
@@ -22,14 +23,17 @@ def lib():
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "pfkv.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pfkv_[a-z_]+)\s*\(", text)))
+    names = set()
+    for header in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pfkv_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_symbols()
-    assert "pfkv_verify_attn_fwd" in names and len(names) >= 7
+    assert {"pfkv_verify_attn_fwd", "pfkv_prefill_fwd", "pfkv_prefill_check_args"} <= set(names)
+    assert len(names) >= 9
     for name in names:
         assert hasattr(lib, name), name
 
@@ -187,3 +191,70 @@ def test_ragged_workload_is_seeded_and_in_range():
     assert w.num_seqs == 8 and all(1 <= q <= 4 for q in w.q_lens)
     assert all(6 <= c <= 105000 and c >= q for c, q in zip(w.ctx, w.q_lens))
     assert w == workload("ragged")
+
+
+# ---------------------------------------------------------------- prefill
+def test_prefill_struct_layout_matches_header(tmp_path):
+    fields = [f for f, _ in binding.PfkvPrefillArgs._fields_]
+    src = tmp_path / "layout_prefill.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"pfkv_prefill.h\"\nint main(void) {\n"
+                   f'  printf("%zu\\n", sizeof(pfkv_prefill_args));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(pfkv_prefill_args, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout_prefill"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(binding.PfkvPrefillArgs)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(binding.PfkvPrefillArgs, f).offset == off, f
+
+
+def _valid_prefill(**over):
+    a = binding.PfkvPrefillArgs()
+    for k, name in enumerate(["q", "k", "v", "out", "cu_seqlens_q", "cu_seqlens_k", "q_descale", "k_descale",
+                              "v_descale"]):
+        setattr(a, name, 0x100000 + 0x10000 * k)
+    a.q_stride_token, a.q_stride_head = 96 * 192, 192
+    a.k_stride_token, a.k_stride_head = 96 * 192, 192
+    a.v_stride_token, a.v_stride_head = 96 * 128, 128
+    a.out_stride_token, a.out_stride_head = 96 * 128, 128
+    a.num_seqs, a.total_q, a.total_k, a.num_q_heads, a.num_kv_heads = 1, 12288, 14336, 96, 96
+    a.head_dim_qk, a.head_dim_v, a.max_seqlen_q = 192, 128, 12288
+    a.softmax_scale, a.causal = 192 ** -0.5, 1
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+PREFILL_CASES = [
+    ("valid", {}, "gfx950", OK),
+    ("non-causal", dict(causal=0), "gfx950", OK),
+    ("with lse", dict(lse=0x1f0000), "gfx950", OK),
+    ("gqa 8", dict(num_kv_heads=12), "gfx950", OK),
+    ("no keys", dict(total_k=0), "gfx950", OK),
+    ("gfx942", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
+    ("head dims 128/128", dict(head_dim_qk=128), "gfx950", UNSUPPORTED),
+    ("v head dim 192", dict(head_dim_v=192), "gfx950", UNSUPPORTED),
+    ("q NULL", dict(q=None), "gfx950", INVALID),
+    ("v_descale NULL", dict(v_descale=None), "gfx950", INVALID),
+    ("zero seqs", dict(num_seqs=0), "gfx950", INVALID),
+    ("too many seqs", dict(num_seqs=70000), "gfx950", INVALID),
+    ("zero q heads", dict(num_q_heads=0), "gfx950", INVALID),
+    ("zero kv heads", dict(num_kv_heads=0), "gfx950", INVALID),
+    ("heads not divisible", dict(num_kv_heads=7), "gfx950", INVALID),
+    ("negative total_k", dict(total_k=-1), "gfx950", INVALID),
+    ("zero max_seqlen_q", dict(max_seqlen_q=0), "gfx950", INVALID),
+    ("nan scale", dict(softmax_scale=float("nan")), "gfx950", INVALID),
+    ("zero scale", dict(softmax_scale=0.0), "gfx950", INVALID),
+    ("q stride not 16", dict(q_stride_head=200), "gfx950", INVALID),
+    ("k stride zero", dict(k_stride_token=0), "gfx950", INVALID),
+    ("out stride odd", dict(out_stride_head=130), "gfx950", INVALID),
+    ("q misaligned", dict(q=0x100008), "gfx950", INVALID),
+    ("out misaligned", dict(out=0x130004), "gfx950", INVALID),
+    ("lse misaligned", dict(lse=0x1f0002), "gfx950", INVALID),
+]
+
+
+@pytest.mark.parametrize("name,over,arch,expect", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_check_args(lib, name, over, arch, expect):
+    assert binding.check_prefill_args(_valid_prefill(**over), arch) == expect, (name, binding.last_error())
