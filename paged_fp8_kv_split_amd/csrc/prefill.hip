@@ -6,11 +6,14 @@
 //
 // * A work-group of 8 waves serves 256 query rows of one (sequence, query
 //   head); wave w owns rows 32 w .. 32 w + 31 whole (no cross-wave softmax).
-// * Key tiles of 64 rows stream HBM/L2 -> LDS through a 3-stage ring with
-//   global_load_lds_dwordx4 (one barrier per tile, two tiles in flight). K rows
-//   (192 bytes) sit at rotated 16-byte positions and V rows (128 bytes) at
+// * Key stages of 128 rows (two 64-key sub-tiles) stream HBM/L2 -> LDS through
+//   a 3-stage ring with global_load_lds_dwordx4 (one barrier per stage, two
+//   stages in flight, five 1 KiB transfers per wave and stage). K rows (192
+//   bytes) sit at rotated 16-byte positions and V rows (128 bytes) at
 //   XOR-swizzled ones, so the MFMA operand reads below are free of bank
 //   conflicts.
+// * The MFMA groups run at raised wave priority, so the two waves of a SIMD
+//   drift apart: one feeds the matrix core while the other does its softmax.
 // * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (three k-steps over the
 //   192 dims), Q held in registers. A lane then holds 32 scores of one query row.
 // * Online softmax in the log2 domain with a lazy reference max (moved only
@@ -45,14 +48,19 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kTileRows = kWaves * kRowsPerWave;      // 256 query rows per work-group
-constexpr int kKeys = 64;                             // keys per tile
+constexpr int kKeys = 64;                             // keys per sub-tile
+constexpr int kSubs = 2;                              // sub-tiles per stage
+constexpr int kStageKeys = kSubs * kKeys;             // 128 keys per stage
 constexpr int kDqk = 192, kDv = 128;
 constexpr int kKBytes = kKeys * kDqk;                 // 12 KiB
 constexpr int kVBytes = kKeys * kDv;                  // 8 KiB
-constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kSubBytes = kKBytes + kVBytes;          // one sub-tile: K then V
+constexpr int kStageBytes = kSubs * kSubBytes;        // 40 KiB
 constexpr int kStages = 3;
 constexpr int kKParts = kKBytes / 1024;               // 12 transfers of 1 KiB
-constexpr int kParts = kKParts + kVBytes / 1024;      // 20 per tile
+constexpr int kSubParts = kKParts + kVBytes / 1024;   // 20 per sub-tile
+constexpr int kPartsPerWave = kSubs * kSubParts / kWaves;   // 5
+static_assert(kSubs * kSubParts == kWaves * kPartsPerWave, "transfers split evenly over the waves");
 constexpr float kLazySlack = 8.0f;
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -114,7 +122,7 @@ prefill_kernel(PrefillParams p) {
   const int rows_end = min(i0 + kTileRows, lq);
   // keys some row of the work-group (the wave) can see
   const int kv_end = CAUSAL ? min(max(lk - lq + rows_end, 0), lk) : lk;
-  const int n_tiles = (kv_end + kKeys - 1) / kKeys;
+  const int n_tiles = (kv_end + kStageKeys - 1) / kStageKeys;   // stages
   const int r0 = i0 + kRowsPerWave * w;              // this wave's first row
   const bool wave_rows = r0 < lq;
   const int kv_end_w = !wave_rows ? 0 : (CAUSAL ? min(max(lk - lq + min(r0 + kRowsPerWave, lq), 0), lk) : lk);
@@ -135,31 +143,40 @@ prefill_kernel(PrefillParams p) {
     }
   }
 
-  // ---- tile transfers: wave w moves parts w, w + 8, w + 16 (< 20) of every tile
+  // ---- stage transfers: wave w moves parts w + 8 j (j < 5) of every stage;
+  // part m is part m mod 20 of sub-tile m / 20 (K parts 0-11, V parts 12-19)
   const uint8_t* kbase = p.k + (int64_t)k0 * p.k_stride_token + (int64_t)hkv * p.k_stride_head;
   const uint8_t* vbase = p.v + (int64_t)k0 * p.v_stride_token + (int64_t)hkv * p.v_stride_head;
   const unsigned ring = lds_addr(smem);
+  int x_key[kPartsPerWave];        // key of this lane's 16 bytes in the stage (0..127)
+  int x_off[kPartsPerWave];        // byte offset inside that key's row
+  bool x_isk[kPartsPerWave];
+#pragma unroll
+  for (int j = 0; j < kPartsPerWave; ++j) {
+    const int m = w + kWaves * j, sub = m / kSubParts, mm = m - kSubParts * sub;
+    if (mm < kKParts) {
+      const int u = 64 * mm + lane;                   // 16-byte unit of the K sub-tile
+      const int key = u / 12, pos = u - 12 * key;
+      x_key[j] = kKeys * sub + key;
+      x_off[j] = 16 * ((pos + 12 - k_rot(key)) % 12);
+      x_isk[j] = true;
+    } else {
+      const int key = 8 * (mm - kKParts) + (lane >> 3), pos = lane & 7;
+      x_key[j] = kKeys * sub + key;
+      x_off[j] = 16 * (pos ^ v_sw(key));
+      x_isk[j] = false;
+    }
+  }
   auto issue = [&](int t) {
-    const int kt = kKeys * t;
+    const int kt = kStageKeys * t;
     const unsigned stage = ring + (t % kStages) * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int m = w + 8 * j;
-      if (m < kKParts) {
-        const int u = 64 * m + lane;                    // 16-byte unit of the K tile
-        const int key = u / 12, pos = u - 12 * key;
-        const int c = (pos + 12 - k_rot(key)) % 12;
-        const int kg = min(kt + key, lk - 1);           // keys past the end read the last (masked)
-        dma_1k_addr(kbase + (int64_t)kg * p.k_stride_token + 16 * c, stage + 1024 * m);
-      } else if (m < kParts) {
-        const int mm = m - kKParts;
-        const int key = 8 * mm + (lane >> 3), pos = lane & 7;
-        const int kg = min(kt + key, lk - 1);
-        dma_1k_addr(vbase + (int64_t)kg * p.v_stride_token + 16 * (pos ^ v_sw(key)), stage + kKBytes + 1024 * mm);
-      }
+    for (int j = 0; j < kPartsPerWave; ++j) {
+      const int kg = min(kt + x_key[j], lk - 1);       // keys past the end read the last (masked)
+      const uint8_t* src = x_isk[j] ? kbase + (int64_t)kg * p.k_stride_token : vbase + (int64_t)kg * p.v_stride_token;
+      dma_1k_addr(src + x_off[j], stage + 1024 * (w + kWaves * j));
     }
   };
-  const bool three = w < kParts - 16;                 // waves 0-3 move three parts, 4-7 two
   if (n_tiles > 0) issue(0);
   if (n_tiles > 1) issue(1);
 
@@ -189,123 +206,128 @@ prefill_kernel(PrefillParams p) {
   float l_lane = 0.f;                  // this lane's share of the row sum
 
   for (int t = 0; t < n_tiles; ++t) {
-    // this wave's transfers of tile t have landed (tile t + 1 may fly), then
-    // everyone's have, and everyone is done with the stage tile t + 2 reuses
-    if (t + 1 < n_tiles) {
-      if (three)
-        asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
+    // this wave's transfers of stage t have landed (stage t + 1 may fly), then
+    // everyone's have, and everyone is done with the stage t + 2 reuses
+    if (t + 1 < n_tiles)
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
     lds_barrier();
     if (t + 2 < n_tiles) issue(t + 2);
-    const int kt = kKeys * t;
-    if (kt >= kv_end_w) continue;                   // every key of the tile is masked for this wave
-    const uint8_t* stage = smem + (t % kStages) * kStageBytes;
+#pragma unroll 1
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const int kt = kStageKeys * t + kKeys * sub;
+      if (kt >= kv_end_w) break;                      // every key from here on is masked for this wave
+      const uint8_t* stage = smem + (t % kStages) * kStageBytes + sub * kSubBytes;
 
-    // scores: s[kb][r] = S^T[key 32 kb + 8 (r >> 2) + 4 h + (r & 3)][row]
-    f32x16 sc[2];
+      // scores: s[kb][r] = S^T[key 32 kb + 8 (r >> 2) + 4 h + (r & 3)][row]
+      f32x16 sc[2];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
-      const int key = 32 * kb + col;
-      const int rot = k_rot(key);
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[kb] = f32x16{};
+        const int key = 32 * kb + col;
+        const int rot = k_rot(key);
 #pragma unroll
-      for (int kc = 0; kc < 3; ++kc) {
-        const int c = 4 * kc + 2 * h;
-        const i32x4 lo = *(const i32x4*)(stage + 16 * (12 * key + (c + rot) % 12));
-        const i32x4 hi = *(const i32x4*)(stage + 16 * (12 * key + (c + 1 + rot) % 12));
-        const i32x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sc[kb] = mfma8(ka, qop[kc], sc[kb], 127, 127);
+        for (int kc = 0; kc < 3; ++kc) {
+          const int c = 4 * kc + 2 * h;
+          const i32x4 lo = *(const i32x4*)(stage + 16 * (12 * key + (c + rot) % 12));
+          const i32x4 hi = *(const i32x4*)(stage + 16 * (12 * key + (c + 1 + rot) % 12));
+          const i32x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          sc[kb] = mfma8(ka, qop[kc], sc[kb], 127, 127);
+        }
       }
-    }
-    // masks: keys past the sequence, and (causal) past the row's diagonal
-    const bool edge = kt + kKeys > lk || (CAUSAL && kt + kKeys - 1 > lk - lq + r0);
-    if (edge) {
-      const int lim = CAUSAL ? min(lk - 1, lk - lq + row) : lk - 1;
+      __builtin_amdgcn_s_setprio(0);
+      // masks: keys past the sequence, and (causal) past the row's diagonal
+      const bool edge = kt + kKeys > lk || (CAUSAL && kt + kKeys - 1 > lk - lq + r0);
+      if (edge) {
+        const int lim = CAUSAL ? min(lk - 1, lk - lq + row) : lk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            sc[kb][r] = key <= lim ? sc[kb][r] : -__builtin_inff();
+          }
+      }
+      // raw-score maxima of the two 32-key blocks and of the row (both lanes of
+      // the row agree on all three)
+      float bmx[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float x = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, sc[kb][r]);
+        bmx[kb] = fmaxf(x, __shfl_xor(x, 32, 64));
+      }
+      const float mx = fmaxf(bmx[0], bmx[1]);
+      const bool move = mx > thr;
+      if (__any(move)) {
+        float alpha = 1.f;
+        if (move) {
+          const float m_new = mx * c2;
+          alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 when m_ref was -inf
+          m_ref = m_new;
+          thr = (m_new + kLazySlack) / c2;
+        }
+        l_lane *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      // P = 2^(s c2 - m) (0 for a masked key) in e4m3 with a power-of-two scale
+      // 2^e per block of 32 keys (block kb: this lane's bytes 16 kb .. + 15 and
+      // its partner lane's): the block's largest P, 2^(bmx c2 - m), sets e so
+      // that it lands in [128, 256), and 2^-e is folded into the exponent.
+      // P never exceeds 2^8 (lazy max), so e <= 1; a block whose largest P is
+      // below 2^-100 contributes nothing and is zeroed (e = 0), so e >= -107.
+      const float mref = m_ref == -__builtin_inff() ? 0.f : m_ref;
+      int eb[2];
+      float shift[2], down[2];
+      bool live[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float top = __builtin_amdgcn_exp2f(__builtin_fmaf(bmx[kb], c2, -mref));
+        live[kb] = top >= 0x1p-100f;
+        eb[kb] = live[kb] ? (int)((__float_as_uint(top) >> 23) & 255) - 127 - 7 : 0;
+        shift[kb] = mref + (float)eb[kb];
+        down[kb] = __uint_as_float((uint32_t)(127 + eb[kb]) << 23);              // 2^e
+      }
+      float pv[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          sc[kb][r] = key <= lim ? sc[kb][r] : -__builtin_inff();
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -shift[kb]));
+          pv[16 * kb + r] = (!live[kb] || (edge && sc[kb][r] == -__builtin_inff())) ? 0.f : x;
         }
-    }
-    // lazy reference max of the row (both lanes of the row agree)
-    float mx = -__builtin_inff();
+      int pw[8];
+      float lsum[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool move = mx > thr;
-    if (__any(move)) {
-      float alpha = 1.f;
-      if (move) {
-        const float m_new = mx * c2;
-        alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 when m_ref was -inf
-        m_ref = m_new;
-        thr = (m_new + kLazySlack) / c2;
+      for (int j = 0; j < 8; ++j) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], word, true);
+        pw[j] = word;
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        const f32x2 bb = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+        lsum[j >> 2] += (a[0] + a[1]) + (bb[0] + bb[1]);
       }
-      l_lane *= alpha;
+      l_lane += lsum[0] * down[0] + lsum[1] * down[1];
+      const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
+      const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+      // O^T += V^T P^T over the sub-tile's 64 keys, four 32-dim tiles
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        i32x2 vr[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    // P = 2^(s c2 - m) (0 for a masked key), then e4m3 with a power-of-two
-    // scale per block of 32 keys (block kb: this lane's bytes 16 kb .. + 15 and
-    // its partner lane's)
-    const float mref = m_ref == -__builtin_inff() ? 0.f : m_ref;
-    float pv[32];
-    float pm[2] = {0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
-        pv[16 * kb + r] = edge && sc[kb][r] == -__builtin_inff() ? 0.f : x;
-        pm[kb] = fmaxf(pm[kb], pv[16 * kb + r]);
+        for (int mm = 0; mm < 4; ++mm)
+          vr[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(stage + v_off[mm][dt]));
+        const i32x8 va = {vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]};
+        o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
       }
-    // block exponent e with pm 2^-e in [128, 256); E8M0 byte 127 + e. P never
-    // exceeds 2^8 (lazy max), so e <= 1; a block whose largest probability is
-    // below 2^-100 contributes nothing and is zeroed (e = 0), so e >= -107.
-    int eb[2];
-    float up[2], down[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float m = fmaxf(pm[kb], __shfl_xor(pm[kb], 32, 64));
-      const bool live = m >= 0x1p-100f;
-      eb[kb] = live ? (int)((__float_as_uint(m) >> 23) & 255) - 127 - 7 : 0;
-      up[kb] = live ? __uint_as_float((uint32_t)(127 - eb[kb]) << 23) : 0.f;   // 2^-e
-      down[kb] = __uint_as_float((uint32_t)(127 + eb[kb]) << 23);              // 2^e
-    }
-    int pw[8];
-    float lsum[2] = {0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = up[j >> 2];
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j] * f, pv[4 * j + 1] * f, 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2] * f, pv[4 * j + 3] * f, word, true);
-      pw[j] = word;
-      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-      const f32x2 bb = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-      lsum[j >> 2] += (a[0] + a[1]) + (bb[0] + bb[1]);
-    }
-    l_lane += lsum[0] * down[0] + lsum[1] * down[1];
-    const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
-    const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    // O^T += V^T P^T over the tile's 64 keys, four 32-dim tiles
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      i32x2 vr[4];
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
-        vr[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(stage + v_off[mm][dt]));
-      const i32x8 va = {vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]};
-      o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 
