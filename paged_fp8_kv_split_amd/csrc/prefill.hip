@@ -23,7 +23,8 @@
 //   [128, 256) before rounding, and the scale rides in the MFMA's B-scale
 //   operand. Small probabilities then keep their 3-bit mantissa instead of
 //   flushing to zero (the underflow the same page's review works through).
-//   The row sum l adds the rounded, rescaled values, so O and the LSE use the
+//   The row sum l is the same MFMA with an all-ones operand in place of V^T, so
+//   it adds the rounded, rescaled values, and O and the LSE use the
 //   same weights. On this MFMA the scale in lane c + 32 kb covers bytes
 //   16 kb .. 16 kb + 15 of both lane halves of column c (measured), which here
 //   are keys 32 kb .. 32 kb + 31 of the row: both lanes of a row share each
@@ -203,7 +204,11 @@ prefill_kernel(PrefillParams p) {
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float m_ref = -__builtin_inff();     // reference max of this lane's row (log2 units)
   float thr = -__builtin_inff();       // raw-score threshold (m_ref + slack) / c2
-  float l_lane = 0.f;                  // this lane's share of the row sum
+  // row sum l = sum of the rounded, block-scaled P, from the matrix core: the
+  // same MFMA as O^T with an all-ones A operand (every element of ol is l)
+  f32x16 ol = f32x16{};
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
   for (int t = 0; t < n_tiles; ++t) {
     // this wave's transfers of stage t have landed (stage t + 1 may fly), then
@@ -241,6 +246,9 @@ prefill_kernel(PrefillParams p) {
       // masks: keys past the sequence, and (causal) past the row's diagonal
       const bool edge = kt + kKeys > lk || (CAUSAL && kt + kKeys - 1 > lk - lq + r0);
       if (edge) {
+        // (the empty volatile asm keeps this a branch: the compiler would
+        // otherwise turn it into per-score selects on every sub-tile)
+        asm volatile("");
         const int lim = CAUSAL ? min(lk - 1, lk - lq + row) : lk - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -270,7 +278,7 @@ prefill_kernel(PrefillParams p) {
           m_ref = m_new;
           thr = (m_new + kLazySlack) / c2;
         }
-        l_lane *= alpha;
+        ol *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -281,39 +289,40 @@ prefill_kernel(PrefillParams p) {
       // its partner lane's): the block's largest P, 2^(bmx c2 - m), sets e so
       // that it lands in [128, 256), and 2^-e is folded into the exponent.
       // P never exceeds 2^8 (lazy max), so e <= 1; a block whose largest P is
-      // below 2^-100 contributes nothing and is zeroed (e = 0), so e >= -107.
+      // below 2^-100 contributes nothing: its shift is +inf, so every P of it
+      // is 2^-inf = 0, and e = 0, so e >= -107. A masked score (-inf) gives
+      // 2^-inf = 0 as well; edge sub-tiles still zero masked keys explicitly,
+      // which keeps them 0 even for a zero descale.
       const float mref = m_ref == -__builtin_inff() ? 0.f : m_ref;
       int eb[2];
-      float shift[2], down[2];
-      bool live[2];
+      float shift[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const float top = __builtin_amdgcn_exp2f(__builtin_fmaf(bmx[kb], c2, -mref));
-        live[kb] = top >= 0x1p-100f;
-        eb[kb] = live[kb] ? (int)((__float_as_uint(top) >> 23) & 255) - 127 - 7 : 0;
-        shift[kb] = mref + (float)eb[kb];
-        down[kb] = __uint_as_float((uint32_t)(127 + eb[kb]) << 23);              // 2^e
+        const bool live = top >= 0x1p-100f;
+        eb[kb] = live ? (int)((__float_as_uint(top) >> 23) & 255) - 127 - 7 : 0;
+        shift[kb] = live ? mref + (float)eb[kb] : __builtin_inff();
       }
       float pv[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -shift[kb]));
-          pv[16 * kb + r] = (!live[kb] || (edge && sc[kb][r] == -__builtin_inff())) ? 0.f : x;
-        }
+        for (int r = 0; r < 16; ++r)
+          pv[16 * kb + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -shift[kb]));
+      if (edge) {
+        asm volatile("");   // a branch, as above
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pv[16 * kb + r] = sc[kb][r] == -__builtin_inff() ? 0.f : pv[16 * kb + r];
+      }
       int pw[8];
-      float lsum[2] = {0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], word, true);
-        pw[j] = word;
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const f32x2 bb = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        lsum[j >> 2] += (a[0] + a[1]) + (bb[0] + bb[1]);
+        pw[j] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], word, true);
       }
-      l_lane += lsum[0] * down[0] + lsum[1] * down[1];
       const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
       const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
       // O^T += V^T P^T over the sub-tile's 64 keys, four 32-dim tiles
@@ -327,13 +336,14 @@ prefill_kernel(PrefillParams p) {
         const i32x8 va = {vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]};
         o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
       }
+      ol = mfma8(ones, pb, ol, 127, 127 + e);
       __builtin_amdgcn_s_setprio(0);
     }
   }
 
   // ---- epilogue: o = O / l (0 without a visible key), bf16 out, optional lse
   if (!wave_rows) return;
-  const float l = l_lane + __shfl_xor(l_lane, 32, 64);
+  const float l = ol[0];
   if (!row_ok) return;
   const float inv = l > 0.f ? *(const const_f32*)p.v_descale / l : 0.f;
   uint16_t* dst = p.out + (int64_t)(q0 + row) * p.out_stride_token + (int64_t)hq * p.out_stride_head;
