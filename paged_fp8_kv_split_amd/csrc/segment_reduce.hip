@@ -13,9 +13,10 @@
 // statistics (aiter PR #7375, Behavior and intent). A sink logit of the row's
 // head adds e^sink to the denominator (and to the lse sum) and nothing to the
 // numerator.
-// One wave per output row: lane s holds (m_s, l_s), lane i dims 4i .. 4i + 3
-// of the fp16 o rows (head dim 128: lanes 0-31), whose loads for up to 16
-// segments are in flight together.
+// One wave per output row, eight rows per work-group (measured 1 us faster per
+// call than four at 16 x 35000: fewer, fuller work-groups): lane s holds
+// (m_s, l_s), lane i dims 4i .. 4i + 3 of the fp16 o rows (head dim 128: lanes
+// 0-31), whose loads for up to 16 segments are in flight together.
 #include "pfkv_internal.h"
 
 namespace pfkv {
@@ -32,11 +33,11 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 
 constexpr int kBatch = 16;   // segments whose o loads fly together
 
-__global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
+__global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t rows_total = (int64_t)p.total_q * p.num_q_heads;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row = (int64_t)blockIdx.x * 8 + wave;
   if (row >= rows_total) return;
   const int S = p.num_segments;
 
@@ -98,8 +99,8 @@ __global__ void __launch_bounds__(256) segment_reduce_kernel(ReduceParams p) {
 
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
-  const dim3 grid((unsigned)((rows + 3) / 4));
-  hipLaunchKernelGGL(segment_reduce_kernel, grid, dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)((rows + 7) / 8));
+  hipLaunchKernelGGL(segment_reduce_kernel, grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
