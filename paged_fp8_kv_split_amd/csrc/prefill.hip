@@ -83,6 +83,14 @@ __device__ __forceinline__ void dma_1k_addr(const uint8_t* addr, unsigned lds) {
       : "memory");
 }
 
+// max(x of lane i, x of lane i ^ 32) in every lane, by one VALU swap of the
+// wave's 32-lane halves (a general shuffle is an LDS round trip). With both
+// operands x, the swap returns (x[i mod 32], x[i mod 32 + 32]) in lane i.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -188,15 +196,26 @@ prefill_kernel(PrefillParams p) {
   // 32 (mm >> 1) + 16 (mm & 1) + 8 (k >> 2) + 4 h + (k & 3); ds_read_b64_tr_b8
   // hands lane n of the group byte k of source lane 2 k + n / 8, so lane
   // (col, h) receives dim 32 dt + col of the keys of k-slots 32 h + 8 mm .. + 7.
-  int v_off[4][4];
+  // The swizzle of a V row depends only on key bits 1 and 3, which the 16-key
+  // steps of mm leave alone, so instruction mm reads at a per-lane base for
+  // tile dt plus the constant (32 (mm >> 1) + 16 (mm & 1)) kDv, which the
+  // instruction's immediate offset carries; likewise a K row's rotation
+  // depends on key bits 2-3 only, so the second 32-key block is the first's
+  // addresses plus 32 kDqk.
+  int v_base[4];
   {
     const int gq = (lane >> 4) & 1, s = lane & 15, k = s >> 1, hb = s & 1;
+    const int key = 8 * (k >> 2) + 4 * h + (k & 3);
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const int key = 32 * (mm >> 1) + 16 * (mm & 1) + 8 * (k >> 2) + 4 * h + (k & 3);
+    for (int dt = 0; dt < 4; ++dt) v_base[dt] = kKBytes + key * kDv + 16 * ((2 * dt + gq) ^ v_sw(key)) + 8 * hb;
+  }
+  int k_off[3][2];   // [kc][half]: chunk 4 kc + 2 h + half of key col, rotated
+  {
+    const int rot = k_rot(col);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) v_off[mm][dt] = kKBytes + key * kDv + 16 * ((2 * dt + gq) ^ v_sw(key)) + 8 * hb;
-    }
+    for (int kc = 0; kc < 3; ++kc)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) k_off[kc][hf] = 16 * (12 * col + (4 * kc + 2 * h + hf + rot) % 12);
   }
 
   f32x16 o[4];
@@ -228,16 +247,18 @@ prefill_kernel(PrefillParams p) {
       // scores: s[kb][r] = S^T[key 32 kb + 8 (r >> 2) + 4 h + (r & 3)][row]
       f32x16 sc[2];
       __builtin_amdgcn_s_setprio(1);
+      const uint8_t* kp[3][2];
+#pragma unroll
+      for (int kc = 0; kc < 3; ++kc)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) kp[kc][hf] = stage + k_off[kc][hf];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sc[kb] = f32x16{};
-        const int key = 32 * kb + col;
-        const int rot = k_rot(key);
 #pragma unroll
         for (int kc = 0; kc < 3; ++kc) {
-          const int c = 4 * kc + 2 * h;
-          const i32x4 lo = *(const i32x4*)(stage + 16 * (12 * key + (c + rot) % 12));
-          const i32x4 hi = *(const i32x4*)(stage + 16 * (12 * key + (c + 1 + rot) % 12));
+          const i32x4 lo = *(const i32x4*)(kp[kc][0] + 32 * kDqk * kb);
+          const i32x4 hi = *(const i32x4*)(kp[kc][1] + 32 * kDqk * kb);
           const i32x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           sc[kb] = mfma8(ka, qop[kc], sc[kb], 127, 127);
         }
@@ -266,7 +287,7 @@ prefill_kernel(PrefillParams p) {
         float x = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 16; ++r) x = fmaxf(x, sc[kb][r]);
-        bmx[kb] = fmaxf(x, __shfl_xor(x, 32, 64));
+        bmx[kb] = pair_max(x);
       }
       const float mx = fmaxf(bmx[0], bmx[1]);
       const bool move = mx > thr;
@@ -320,7 +341,9 @@ prefill_kernel(PrefillParams p) {
       int pw[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], 0, false);
+        // both 16-bit halves are written, so the word's prior value is free:
+        // seeding it with an input avoids a register clear per word
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], __float_as_int(pv[4 * j]), false);
         pw[j] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], word, true);
       }
       const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
@@ -329,11 +352,14 @@ prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
+        const uint8_t* vp = stage + v_base[dt];
         i32x2 vr[4];
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm)
-          vr[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(stage + v_off[mm][dt]));
-        const i32x8 va = {vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]};
+          vr[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + (32 * (mm >> 1) + 16 * (mm & 1)) * kDv));
+        const i32x4 v01 = __builtin_shufflevector(vr[0], vr[1], 0, 1, 2, 3);
+        const i32x4 v23 = __builtin_shufflevector(vr[2], vr[3], 0, 1, 2, 3);
+        const i32x8 va = __builtin_shufflevector(v01, v23, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
       }
       ol = mfma8(ones, pb, ol, 127, 127 + e);
