@@ -319,9 +319,10 @@ prefill_kernel(PrefillParams p) {
       float shift[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float top = __builtin_amdgcn_exp2f(__builtin_fmaf(bmx[kb], c2, -mref));
-        const bool live = top >= 0x1p-100f;
-        eb[kb] = live ? (int)((__float_as_uint(top) >> 23) & 255) - 127 - 7 : 0;
+        // log2 of the block's largest P; e = floor of it - 7 puts that P in [128, 256)
+        const float top2 = __builtin_fmaf(bmx[kb], c2, -mref);
+        const bool live = top2 >= -100.f;
+        eb[kb] = live ? (int)__builtin_floorf(top2) - 7 : 0;
         shift[kb] = live ? mref + (float)eb[kb] : __builtin_inff();
       }
       float pv[32];
