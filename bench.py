@@ -260,7 +260,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the path runs on one GPU; across GPUs it would shard by sequence or KV head with no "
+              "communication, or by KV segment with one gather of the partials before the reduce)", file=sys.stderr)
         sys.exit(2)
 
     import torch
