@@ -150,6 +150,10 @@ prefill_kernel(PrefillParams p) {
       const i32x4 hi = *(const i32x4*)(qrow + 64 * kc + 32 * h + 16);
       qop[kc] = row_ok ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]} : i32x8{};
     }
+    // Consume Q here, so the compiler waits for these loads now. Left pending,
+    // its wait would sit in the key loop as a full vmcnt(0), which also counts
+    // the LDS transfers of the stages in flight and would drain the ring there.
+    asm volatile("" ::"v"(qop[0]), "v"(qop[1]), "v"(qop[2]));
   }
 
   // ---- stage transfers: wave w moves parts w + 8 j (j < 5) of every stage;
