@@ -230,7 +230,8 @@ prefill_kernel(PrefillParams p) {
   // row sum l = sum of the rounded, block-scaled P, from the matrix core: the
   // same MFMA as O^T with an all-ones A operand (every element of ol is l)
   f32x16 ol = f32x16{};
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+  i32x8 pb = {};   // P^T operand of the current sub-tile: e4m3 bytes of this lane's row
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -343,16 +344,15 @@ prefill_kernel(PrefillParams p) {
           for (int r = 0; r < 16; ++r)
             pv[16 * kb + r] = sc[kb][r] == -__builtin_inff() ? 0.f : pv[16 * kb + r];
       }
-      int pw[8];
+      // packed in place into the MFMA operand (loop-carried, so its registers
+      // stay one tuple); both 16-bit halves of each word are written, so the
+      // word's prior value is free
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // both 16-bit halves are written, so the word's prior value is free:
-        // seeding it with an input avoids a register clear per word
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], __float_as_int(pv[4 * j]), false);
-        pw[j] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], word, true);
+        pb[j] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j], pv[4 * j + 1], pb[j], false);
+        pb[j] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * j + 2], pv[4 * j + 3], pb[j], true);
       }
       const int e = h == 0 ? eb[0] : eb[1];   // the scale this lane supplies
-      const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
       // O^T += V^T P^T over the sub-tile's 64 keys, four 32-dim tiles
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -367,6 +367,9 @@ prefill_kernel(PrefillParams p) {
         const i32x8 va = __builtin_shufflevector(v01, v23, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = mfma8(va, pb, o[dt], 127, 127 + e);
       }
+      // (the empty asm makes ones opaque, so it stays resident in registers
+      // across sub-tiles instead of being rebuilt by moves every time)
+      asm volatile("" : "+v"(ones));
       ol = mfma8(ones, pb, ol, 127, 127 + e);
       __builtin_amdgcn_s_setprio(0);
     }
