@@ -63,6 +63,7 @@ constexpr int kSubParts = kKParts + kVBytes / 1024;   // 20 per sub-tile
 constexpr int kPartsPerWave = kSubs * kSubParts / kWaves;   // 5
 static_assert(kSubs * kSubParts == kWaves * kPartsPerWave, "transfers split evenly over the waves");
 constexpr float kLazySlack = 8.0f;
+constexpr int kCausalBands = 4;
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -115,8 +116,23 @@ prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
-  const int b = blockIdx.z, hq = blockIdx.y;
-  const int qt = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;   // long tiles first
+  const int b = blockIdx.z;
+  int hq = blockIdx.y, qt = blockIdx.x;
+  if (CAUSAL) {
+    // Causal tiles differ in length (the last query tile sees every key). In
+    // dispatch order, the tiles go in kCausalBands bands of decreasing length,
+    // each band head-major: long work first and short work last across all
+    // heads (no long tile starts near the end), while the work-groups in
+    // flight still share a band's worth of heads' K/V in the caches.
+    const int nt = gridDim.x, nh = gridDim.y;
+    const int lin = blockIdx.x + nt * blockIdx.y;
+    const int tpb = (nt + kCausalBands - 1) / kCausalBands;   // tiles per band
+    const int band = lin / (nh * tpb);
+    const int r = lin - nh * tpb * band;
+    const int sz = min(tpb, nt - band * tpb);                 // tiles in this band
+    hq = r / sz;
+    qt = nt - 1 - (band * tpb + r % sz);                      // rank 0: the longest tile
+  }
 
   // sequence geometry, clamped so that every access stays inside the buffers
   const const_i32* cq = (const const_i32*)p.cu_seqlens_q;
