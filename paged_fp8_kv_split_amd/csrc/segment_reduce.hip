@@ -62,43 +62,67 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// PARTS waves merge one row: wave part q sums the numerator over its share
+// of the segments (at most kBatch, so its o loads go out together), every part
+// computes the same M and denominator from all (m, l), and part 0 adds the
+// parts in order q = 0, 1, ... through LDS and writes the row. With many
+// segments and few rows (4 sequences x 64 segments: 256 rows) one wave per
+// row would load its segments in several dependent batches on a few CUs.
+// PARTS = 1 is one wave per row, the segments summed in order s = 0, 1, ...
+template <int PARTS>
 __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
+  constexpr int kRowsPerWg = 8 / PARTS;
+  __shared__ f32x4 partial[PARTS > 1 ? 8 : 1][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t rows_total = (int64_t)p.total_q * p.num_q_heads;
-  const int64_t row = (int64_t)blockIdx.x * 8 + wave;
-  if (row >= rows_total) return;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + wave / PARTS;
+  const int part = wave % PARTS;
+  const bool valid = row < rows_total;
+  if (PARTS == 1 && !valid) return;
   const int S = p.num_segments;
+  const int per = (S + PARTS - 1) / PARTS;
+  const int sb = min(part * per, S), se = min(sb + per, S);   // this wave's segments
 
-  // the o loads of the first segments go out before (m, l) is known
   const bool dims = 4 * lane < p.head_dim;   // this lane's dims exist
-  const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
-  const int64_t seg_stride = rows_total * kHeadDim;
-  f16x4 a[kBatch];
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k)
-    a[k] = (k < S && dims) ? __builtin_nontemporal_load((const f16x4*)(o + k * seg_stride)) : f16x4{};
-
-  float m = -__builtin_inff(), l = 0.f;
-  if (lane < S) {
-    const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
-    m = v[0];
-    l = v[1];
-  }
-  const float M = wave_max(m);
-  const float coef = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * l;
-  float den = wave_sum(coef);
-
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    if (s0 > 0) {
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        if (s0 + k < S && dims) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
-    }
+  float M = -__builtin_inff(), den = 0.f;
+  if (valid) {
+    // the o loads of the first segments go out before (m, l) is known
+    const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
+    const int64_t seg_stride = rows_total * kHeadDim;
+    f16x4 a[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (s0 + k < S) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
+      a[k] = (sb + k < se && dims) ? __builtin_nontemporal_load((const f16x4*)(o + (sb + k) * seg_stride)) : f16x4{};
+
+    float m = -__builtin_inff(), l = 0.f;
+    if (lane < S) {
+      const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
+      m = v[0];
+      l = v[1];
+    }
+    M = wave_max(m);
+    const float coef = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * l;
+    den = wave_sum(coef);
+
+    for (int s0 = sb; s0 < se; s0 += kBatch) {
+      if (s0 > sb) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+          if (s0 + k < se && dims) a[k] = __builtin_nontemporal_load((const f16x4*)(o + (s0 + k) * seg_stride));
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (s0 + k < se) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
+    }
+  }
+  if constexpr (PARTS > 1) {
+    partial[wave][lane] = num;
+    __syncthreads();
+    if (!valid || part != 0) return;
+#pragma unroll
+    for (int q = 1; q < PARTS; ++q) num += partial[wave + q][lane];
   }
   const int64_t t = row / p.num_q_heads, hq = row - t * p.num_q_heads;
   // a sink logit (log2 units here) joins the denominator: with Mx = max(M, sink),
@@ -124,8 +148,13 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
 
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
-  const dim3 grid((unsigned)((rows + 7) / 8));
-  hipLaunchKernelGGL(segment_reduce_kernel, grid, dim3(512), 0, stream, p);
+  // waves per row: one up to 16 segments (a single batch of loads), else 2 or 4
+  if (p.num_segments <= 16)
+    hipLaunchKernelGGL(segment_reduce_kernel<1>, dim3((unsigned)((rows + 7) / 8)), dim3(512), 0, stream, p);
+  else if (p.num_segments <= 32)
+    hipLaunchKernelGGL(segment_reduce_kernel<2>, dim3((unsigned)((rows + 3) / 4)), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL(segment_reduce_kernel<4>, dim3((unsigned)((rows + 1) / 2)), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
