@@ -67,8 +67,10 @@ def test_gqa8_three_seqs_parity():
     assert_parity(out, oracle_for(case), "gqa8 3x8000")
 
 
-@pytest.mark.parametrize("segments", [1, 2, 3, 7, 16, 64])
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 16, 17, 24, 33, 40, 64])
 def test_segment_count_independence(segments):
+    # 17-32 segments: the reduce merges each row with two waves, 33-64 with four
+    # (uneven shares at 17, 33 and 40)
     w = Workload(name="s", ctx=(8000, 1234, 31), q_lens=(4, 2, 1), num_q_heads=16, num_kv_heads=1,
                  num_segments=segments, seed=32)
     case = make_case(w, "cpu").to(DEV)
@@ -176,7 +178,7 @@ def test_rerun_bitwise():
         assert torch.equal(a.view(torch.int16), o.view(torch.int16))
 
 
-@pytest.mark.parametrize("group,segments", [(16, 8), (8, 8), (16, 1)])
+@pytest.mark.parametrize("group,segments", [(16, 8), (8, 8), (16, 1), (16, 40)])
 def test_short_qlen_rows_match_verify_bitwise(group, segments):
     """Draft-extend (q_len 1..3) and decode rows equal the verify call's rows bit for bit
     (with one segment, through the main kernel's direct bf16 output)."""
