@@ -252,6 +252,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--segments", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--balance", action="store_true",
+                    help="balanced segments (in proportion to each sequence's pages; --segments is the cap, 64 by default)")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--precision", choices=list(PRECISIONS), default="16bit",
                     help="arithmetic of the timed path (the others are timed too, as variants)")
@@ -280,7 +282,7 @@ def main():
     arch, cus = binding.device_info(0)
     w = workload(args.workload)
     R = args.replicas or w.replicas
-    S = args.segments or w.num_segments or pfkv.num_segments(cus, w.num_seqs, w.num_kv_heads)
+    S = args.segments or (64 if args.balance else (w.num_segments or pfkv.num_segments(cus, w.num_seqs, w.num_kv_heads)))
     log(f"device {arch}, {cus} CUs; workload {w.name}: {w.num_seqs} seqs, ctx {w.ctx[:4]}..., "
         f"q_lens {w.q_lens[:4]}..., Hq {w.num_q_heads} / Hkv {w.num_kv_heads}, S={S}, replicas={R}")
 
@@ -294,7 +296,8 @@ def main():
     ws = torch.empty(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device="cuda")
     def make_refs(prec):
         argv = [binding.build_args(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.cu_seqlens_q,
-                                   c.k_descale, c.v_descale, c.softmax_scale, S, out, ws, prec) for c in cases]
+                                   c.k_descale, c.v_descale, c.softmax_scale, S, out, ws, prec,
+                                   balance_segments=args.balance) for c in cases]
         return argv, [ctypes.byref(a) for a in argv]
 
     argv, refs = make_refs(PRECISIONS[args.precision][0])
@@ -453,6 +456,7 @@ def main():
                         f"{w.num_q_heads} q heads / {w.num_kv_heads} kv head(s), head_dim {w.head_dim}, "
                         f"page {w.page_size} NHD fp8 e4m3, per-tensor descales",
             "num_segments": S,
+            "balanced_segments": bool(args.balance),
             "replicas": R,
             "kv_bytes_per_call": w.kv_bytes,
             "device": arch,

@@ -84,7 +84,21 @@ typedef struct pfkv_args {
   float softcap;               /* > 0: every score s becomes softcap * tanh(s / softcap); 0: off */
   int32_t max_q_len;           /* bound on every n_b: 0 (the zero-initialised default) = 4, the pages'
                                   bound; up to 8 (longer drafts); rows of tokens past it are not written */
+  int32_t balance_segments;    /* 0 (default): every sequence is cut into num_segments segments. 1: segments
+                                  in proportion to each sequence's pages (see below); num_segments (2..64)
+                                  is then the cap per sequence and num_seqs must be <= 1024 */
 } pfkv_args;
+
+/*
+ * Balanced segments (balance_segments = 1), for batches whose contexts differ
+ * widely (draft extend and decode): the launch has about one work-group per
+ * CU, `slots` = max(num_seqs, CUs / work-groups per (sequence, segment)) of
+ * them, and sequence b, whose segments split span_b pages, gets
+ * min(num_segments, 1 + floor((slots - num_seqs) span_b / sum of spans))
+ * segments. The schedule is computed on the device from seq_lens (so the call
+ * stays capturable); a sequence's result depends on the other sequences'
+ * lengths through it, not on their queries.
+ */
 
 /*
  * Options that the pages name only as features their gates leave out (SGLang

@@ -105,6 +105,7 @@ class PfkvArgs(ctypes.Structure):
         ("window_keys", ctypes.c_int32),
         ("softcap", ctypes.c_float),
         ("max_q_len", ctypes.c_int32),
+        ("balance_segments", ctypes.c_int32),
     ]
 
 
@@ -205,7 +206,7 @@ PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
 
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None,
-               sinks=None, window_left=-1, softcap=0.0, max_q_len=0) -> PfkvArgs:
+               sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=0) -> PfkvArgs:
     """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here).
 
     ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device,
@@ -277,13 +278,14 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.window_keys = int(window_left) + 1 if window_left >= 0 else 0   # left window W -> W + 1 keys
     a.softcap = float(softcap)
     a.max_q_len = int(max_q_len)
+    a.balance_segments = 1 if balance_segments else 0
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                 softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
                 precision=PRECISION_16BIT, return_lse=False, lse=None, sinks=None, window_left=-1,
-                softcap=0.0, max_q_len=0):
+                softcap=0.0, max_q_len=0, balance_segments=False):
     """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``), or
     ``(out, lse)`` when ``return_lse`` is set or an ``lse`` buffer is given.
 
@@ -294,6 +296,8 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     ``softcap`` (> 0 to enable) are the options described in ``include/pfkv.h``.
     ``max_q_len`` bounds every sequence's query tokens (0 = 4, at most 8).
     ``num_segments=None`` picks the library heuristic from the device's CU count.
+    ``balance_segments=True`` gives each sequence segments in proportion to its
+    pages, with ``num_segments`` as the cap per sequence (``None``: 64).
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
     ``workspace`` (uint8, at least :func:`workspace_bytes` bytes) is allocated with
@@ -304,8 +308,11 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     if not q.is_cuda:
         raise ValueError("q must be a GPU tensor")
     if num_segments is None:
-        _, cus = device_info(q.device.index)
-        num_segments = num_segments_for(cus, seq_lens.numel(), k_cache.shape[2])
+        if balance_segments:
+            num_segments = 64
+        else:
+            _, cus = device_info(q.device.index)
+            num_segments = num_segments_for(cus, seq_lens.numel(), k_cache.shape[2])
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
@@ -315,7 +322,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                    softmax_scale, num_segments, out, workspace, precision, lse, sinks, window_left, softcap,
-                   max_q_len)
+                   max_q_len, balance_segments)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -174,6 +174,9 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
 
   if (a->num_seqs < 1 || a->num_seqs > (1 << 20)) return fail(PFKV_INVALID, "num_seqs must be in [1, 2^20]");
   if (a->total_q < 1) return fail(PFKV_INVALID, "total_q must be >= 1");
+  if (a->balance_segments != 0 && a->balance_segments != 1) return fail(PFKV_INVALID, "balance_segments must be 0 or 1");
+  if (a->balance_segments && (a->num_segments < 2 || a->num_seqs > 1024))
+    return fail(PFKV_INVALID, "balanced segments need num_segments (the cap) >= 2 and num_seqs <= 1024");
   if (a->max_q_len < 0 || a->max_q_len > pfkv::kMaxQLen)
     return fail(PFKV_INVALID, "max_q_len must be in [0, 8] (0 = 4)");
   const int max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
@@ -335,6 +338,13 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   m.token_pages = a->page_size == 1 ? 1 : 0;
   m.max_seq_len = a->max_pages_per_seq * a->page_size;   // <= 2^30 (checked)
   m.num_segments = a->num_segments;
+  m.balance = a->balance_segments;
+  m.num_slots = 0;
+  if (m.balance) {
+    // about one work-group per CU: slots x (work-groups per slot along z)
+    const int per_slot = a->num_kv_heads * m.kv_split * m.q_split;
+    m.num_slots = std::max(a->num_seqs, std::max(1, d.num_cus / per_slot));
+  }
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
 
   rp->ws_o = ws_o;
@@ -349,6 +359,13 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
   rp->num_q_heads = a->num_q_heads;
   rp->num_segments = a->num_segments;
   rp->head_dim = a->head_dim;
+  rp->balance = m.balance;
+  rp->num_slots = m.num_slots;
+  rp->num_seqs = a->num_seqs;
+  rp->window_left = m.window_left;
+  rp->max_seq_len = m.max_seq_len;
+  rp->seq_lens = a->seq_lens;
+  rp->cu_seqlens_q = a->cu_seqlens_q;
   (void)group;
   return PFKV_OK;
 }

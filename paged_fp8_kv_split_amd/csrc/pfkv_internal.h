@@ -58,6 +58,10 @@ struct MainParams {
   int32_t head_dim;            // 256 or 128
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, num_pages, num_segments;
   float score_scale_log2;      // softmax_scale * log2(e); multiplied by *k_descale on the device
+  // balanced segments: blockIdx.x is a slot of gridDim.x (>= num_seqs); each
+  // sequence gets segment_count() of them (num_segments is the cap), the slots
+  // in sequence order; blockIdx.y is 0 and slots past the last one stay idle
+  int32_t balance, num_slots;
 };
 
 struct ReduceParams {
@@ -70,7 +74,36 @@ struct ReduceParams {
   const float* sinks;          // optional [Hq] fp32 sink logits
   int32_t total_q, num_q_heads, num_segments;
   int32_t head_dim;            // 256 or 128 (o rows keep the kHeadDim stride)
+  // balanced segments (see MainParams): a row of sequence b merges
+  // segment_count(b) partials; these are the main kernel's inputs to it
+  int32_t balance, num_slots, num_seqs, window_left, max_seq_len;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
 };
+
+// Pages (16-token blocks) that the segments of a sequence of L keys split:
+// with a left window of W positions, only those from the first page some query
+// can see (bounded with the largest q_len, so independent of the call's q_len).
+__device__ __forceinline__ int segment_span(int L, int window_left) {
+  const int pages = (L + kPageSize - 1) / kPageSize;
+  const int win = window_left < 0 ? -1 : min(window_left, L);
+  const int first = win < 0 ? 0 : min(max(L - kMaxQLen - win, 0) / kPageSize, pages);
+  return pages - first;
+}
+
+// Balanced segments: of `slots` work-group slots, a sequence whose span is
+// `span` pages out of `total` gets 1 + floor((slots - num_seqs) span / total),
+// at most `cap`; the counts add up to at most `slots`. Every input comes from
+// device data and call arguments, so the schedule is the same on every replay.
+__device__ __forceinline__ int segment_count(int span, int64_t total, int slots, int num_seqs, int cap) {
+  const int64_t extra = total > 0 ? (int64_t)(slots - num_seqs) * span / total : 0;
+  return (int)min((int64_t)cap, 1 + extra);
+}
+
+// The clamped KV length of sequence b, as the main kernel reads it.
+__device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int max_seq_len) {
+  return min(max(((__attribute__((address_space(4))) const int32_t*)seq_lens)[b], 0), max_seq_len);
+}
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
 __device__ __forceinline__ uint32_t bf16_rne(float x) {

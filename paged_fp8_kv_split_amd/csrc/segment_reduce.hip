@@ -80,7 +80,24 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   const int part = wave % PARTS;
   const bool valid = row < rows_total;
   if (PARTS == 1 && !valid) return;
-  const int S = p.num_segments;
+  int S = p.num_segments;
+  if (p.balance && valid) {
+    // the row's sequence and its segment count, as the main kernel scheduled them
+    const int t = (int)(row / p.num_q_heads);
+    const __attribute__((address_space(4))) int32_t* cu = (const __attribute__((address_space(4))) int32_t*)p.cu_seqlens_q;
+    int b = -1;
+    for (int i = 0; i < p.num_seqs; ++i)
+      if (t >= cu[i] && t < cu[i + 1]) {
+        b = i;
+        break;
+      }
+    if (b >= 0) {
+      int64_t total = 0;
+      for (int i = 0; i < p.num_seqs; ++i) total += segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left);
+      S = segment_count(segment_span(clamped_len(p.seq_lens, b, p.max_seq_len), p.window_left), total, p.num_slots,
+                        p.num_seqs, p.num_segments);
+    }
+  }
   const int per = (S + PARTS - 1) / PARTS;
   const int sb = min(part * per, S), se = min(sb + per, S);   // this wave's segments
 

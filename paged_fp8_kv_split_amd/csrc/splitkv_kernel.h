@@ -1166,6 +1166,27 @@ splitkv_main_kernel(MainParams p) {
   Geo geo;
   geo.seg = blockIdx.x;
   geo.b = blockIdx.y;
+  int seg_count = p.num_segments;
+  if (p.balance) {
+    // slot blockIdx.x -> (sequence, segment) by the balanced schedule; idle
+    // slots past the last sequence's segments return before any barrier
+    int64_t total = 0;
+    for (int i = 0; i < p.num_seqs; ++i) total += segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left);
+    int acc = 0;
+    geo.b = -1;
+    for (int i = 0; i < p.num_seqs; ++i) {
+      const int n_i = segment_count(segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left), total,
+                                    (int)gridDim.x, p.num_seqs, p.num_segments);
+      if ((int)blockIdx.x < acc + n_i) {
+        geo.b = i;
+        geo.seg = blockIdx.x - acc;
+        seg_count = n_i;
+        break;
+      }
+      acc += n_i;
+    }
+    if (geo.b < 0) return;
+  }
   geo.h = blockIdx.z / p.q_split;
   geo.hkv = geo.h / p.kv_split;
   // out-of-contract values are clamped so that every access stays in its buffer
@@ -1186,9 +1207,9 @@ splitkv_main_kernel(MainParams p) {
   // the first page is bounded with the largest q_len, so that the partition,
   // and with it every row's bits, does not depend on the call's q_len
   geo.win = p.window_left < 0 ? -1 : min(p.window_left, geo.L);
-  const int first = geo.win < 0 ? 0 : min(max(geo.L - kMaxQLen - geo.win, 0) / kPageSize, pages);
-  const int span = pages - first;
-  const int chunk = (span + p.num_segments - 1) / p.num_segments;
+  const int span = segment_span(geo.L, p.window_left);
+  const int first = pages - span;
+  const int chunk = (span + seg_count - 1) / seg_count;
   geo.pb = first + min(geo.seg * chunk, span);
   geo.pe = first + min(geo.seg * chunk + chunk, span);
   geo.rows = G * q_len;
@@ -1221,7 +1242,9 @@ splitkv_main_kernel(MainParams p) {
 // TOK: one-token cache pages; D: head dim
 template <int MODE, bool TOK, int D>
 hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
-  const dim3 grid(p.num_segments, p.num_seqs, p.num_kv_heads * p.kv_split * p.q_split);
+  // balanced: p.num_slots slots along x (see MainParams), else segments x sequences
+  const dim3 grid(p.balance ? p.num_slots : p.num_segments, p.balance ? 1 : p.num_seqs,
+                  p.num_kv_heads * p.kv_split * p.q_split);
   if (group == 16)
     hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
   else if (group == 8)

@@ -89,6 +89,10 @@ CASES = [
     ("zero seqs", dict(num_seqs=0), "gfx950", INVALID),
     ("too many queries", dict(total_q=65), "gfx950", INVALID),
     ("max_q_len 8", dict(max_q_len=8, total_q=128, workspace_size=pfkv.workspace_bytes(16, 128, 16)), "gfx950", OK),
+    ("balanced", dict(balance_segments=1), "gfx950", OK),
+    ("balanced, cap 1", dict(balance_segments=1, num_segments=1, workspace_size=pfkv.workspace_bytes(1, 64, 16)),
+     "gfx950", INVALID),
+    ("balance flag 2", dict(balance_segments=2), "gfx950", INVALID),
     ("max_q_len 8 too many queries", dict(max_q_len=8, total_q=129), "gfx950", INVALID),
     ("max_q_len 9", dict(max_q_len=9), "gfx950", INVALID),
     ("max_q_len negative", dict(max_q_len=-1), "gfx950", INVALID),
