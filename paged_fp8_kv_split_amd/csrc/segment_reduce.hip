@@ -69,7 +69,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // segments and few rows (4 sequences x 64 segments: 256 rows) one wave per
 // row would load its segments in several dependent batches on a few CUs.
 // PARTS = 1 is one wave per row, the segments summed in order s = 0, 1, ...
-template <int PARTS>
+template <int PARTS, bool BAL>
 __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   constexpr int kRowsPerWg = 8 / PARTS;
   __shared__ f32x4 partial[PARTS > 1 ? 8 : 1][64];
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   const bool valid = row < rows_total;
   if (PARTS == 1 && !valid) return;
   int S = p.num_segments;
-  if (p.balance && valid) {
+  if (BAL && valid) {
     // the row's sequence and its segment count, as the main kernel scheduled them
     const int t = (int)(row / p.num_q_heads);
     const __attribute__((address_space(4))) int32_t* cu = (const __attribute__((address_space(4))) int32_t*)p.cu_seqlens_q;
@@ -166,12 +166,20 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   // waves per row: one up to 16 segments (a single batch of loads), else 2 or 4
-  if (p.num_segments <= 16)
-    hipLaunchKernelGGL(segment_reduce_kernel<1>, dim3((unsigned)((rows + 7) / 8)), dim3(512), 0, stream, p);
-  else if (p.num_segments <= 32)
-    hipLaunchKernelGGL(segment_reduce_kernel<2>, dim3((unsigned)((rows + 3) / 4)), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL(segment_reduce_kernel<4>, dim3((unsigned)((rows + 1) / 2)), dim3(512), 0, stream, p);
+  // (balanced segments: a separate instantiation that finds each row's count)
+  if (p.num_segments <= 16) {
+    const dim3 grid((unsigned)((rows + 7) / 8));
+    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<1, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<1, false>), grid, dim3(512), 0, stream, p);
+  } else if (p.num_segments <= 32) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<2, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<2, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    const dim3 grid((unsigned)((rows + 1) / 2));
+    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<4, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<4, false>), grid, dim3(512), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -1155,7 +1155,7 @@ __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& g
 }
 
 // TOK: the cache has one-token pages; D: head dim
-template <int G, int MODE, bool TOK, int D>
+template <int G, int MODE, bool TOK, int D, bool BAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
   using C = Cfg<G, D>;
@@ -1166,8 +1166,10 @@ splitkv_main_kernel(MainParams p) {
   Geo geo;
   geo.seg = blockIdx.x;
   geo.b = blockIdx.y;
+  // BAL: balanced segments (a separate instantiation, so that the default
+  // kernel's code does not carry the schedule)
   int seg_count = p.num_segments;
-  if (p.balance) {
+  if constexpr (BAL) {
     // slot blockIdx.x -> (sequence, segment) by the balanced schedule; idle
     // slots past the last sequence's segments return before any barrier
     int64_t total = 0;
@@ -1245,14 +1247,25 @@ hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
   // balanced: p.num_slots slots along x (see MainParams), else segments x sequences
   const dim3 grid(p.balance ? p.num_slots : p.num_segments, p.balance ? 1 : p.num_seqs,
                   p.num_kv_heads * p.kv_split * p.q_split);
-  if (group == 16)
-    hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 8)
-    hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
-  else if (group == 4)
-    hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D>), grid, dim3(kThreads), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
+  if (p.balance) {
+    if (group == 16)
+      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+    else if (group == 8)
+      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+    else if (group == 4)
+      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    if (group == 16)
+      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+    else if (group == 8)
+      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+    else if (group == 4)
+      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
