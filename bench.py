@@ -253,7 +253,7 @@ def main():
     ap.add_argument("--segments", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--balance", action="store_true",
-                    help="balanced segments (in proportion to each sequence's pages; --segments is the cap, 64 by default)")
+                    help="balanced segments (in proportion to each sequence's pages; --segments is the cap, 128 by default)")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--precision", choices=list(PRECISIONS), default="16bit",
                     help="arithmetic of the timed path (the others are timed too, as variants)")
@@ -282,7 +282,7 @@ def main():
     arch, cus = binding.device_info(0)
     w = workload(args.workload)
     R = args.replicas or w.replicas
-    S = args.segments or (64 if args.balance else (w.num_segments or pfkv.num_segments(cus, w.num_seqs, w.num_kv_heads)))
+    S = args.segments or (128 if args.balance else (w.num_segments or pfkv.num_segments(cus, w.num_seqs, w.num_kv_heads)))
     log(f"device {arch}, {cus} CUs; workload {w.name}: {w.num_seqs} seqs, ctx {w.ctx[:4]}..., "
         f"q_lens {w.q_lens[:4]}..., Hq {w.num_q_heads} / Hkv {w.num_kv_heads}, S={S}, replicas={R}")
 

@@ -85,7 +85,7 @@ typedef struct pfkv_args {
   int32_t max_q_len;           /* bound on every n_b: 0 (the zero-initialised default) = 4, the pages'
                                   bound; up to 8 (longer drafts); rows of tokens past it are not written */
   int32_t balance_segments;    /* 0 (default): every sequence is cut into num_segments segments. 1: segments
-                                  in proportion to each sequence's pages (see below); num_segments (2..64)
+                                  in proportion to each sequence's pages (see below); num_segments (2..128)
                                   is then the cap per sequence and num_seqs must be <= 1024 */
 } pfkv_args;
 

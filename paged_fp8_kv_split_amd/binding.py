@@ -297,7 +297,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     ``max_q_len`` bounds every sequence's query tokens (0 = 4, at most 8).
     ``num_segments=None`` picks the library heuristic from the device's CU count.
     ``balance_segments=True`` gives each sequence segments in proportion to its
-    pages, with ``num_segments`` as the cap per sequence (``None``: 64).
+    pages, with ``num_segments`` as the cap per sequence (``None``: 128).
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
     ``workspace`` (uint8, at least :func:`workspace_bytes` bytes) is allocated with
@@ -309,7 +309,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
         raise ValueError("q must be a GPU tensor")
     if num_segments is None:
         if balance_segments:
-            num_segments = 64
+            num_segments = 128
         else:
             _, cus = device_info(q.device.index)
             num_segments = num_segments_for(cus, seq_lens.numel(), k_cache.shape[2])

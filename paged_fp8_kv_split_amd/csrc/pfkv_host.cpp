@@ -190,8 +190,8 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (a->max_pages_per_seq > (1 << 26)) return fail(PFKV_INVALID, "max_pages_per_seq must be <= 2^26");
   if (a->block_table_stride < a->max_pages_per_seq)
     return fail(PFKV_INVALID, "block_table_stride < max_pages_per_seq");
-  if (a->num_segments < 1 || a->num_segments > pfkv::kMaxSegments)
-    return fail(PFKV_INVALID, "num_segments must be in [1, 64]");
+  if (a->num_segments < 1 || a->num_segments > (a->balance_segments == 1 ? pfkv::kMaxBalancedSegments : pfkv::kMaxSegments))
+    return fail(PFKV_INVALID, "num_segments must be in [1, 64] (a cap of up to 128 with balanced segments)");
   if (a->precision != PFKV_PRECISION_16BIT && a->precision != PFKV_PRECISION_FP8_P &&
       a->precision != PFKV_PRECISION_FP8)
     return fail(PFKV_INVALID, "precision must be one of PFKV_PRECISION_16BIT, _FP8_P, _FP8");

@@ -12,6 +12,7 @@ constexpr int kMaxQLen = 8;     // query tokens per sequence (the pages' 4, or u
 constexpr int kDefaultMaxQLen = 4;
 constexpr int kMaxRows = 64;    // stacked query rows (G x tokens) per work-group
 constexpr int kMaxSegments = 64;
+constexpr int kMaxBalancedSegments = 128;   // the cap per sequence with balanced segments
 
 // Workspace layout, written by the main kernel and read by the reduce:
 //   o  [S][T][Hq][256] fp16  the segment's softmax-weighted mean of V (V without

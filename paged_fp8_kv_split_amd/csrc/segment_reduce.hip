@@ -72,6 +72,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int PARTS, bool BAL>
 __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   constexpr int kRowsPerWg = 8 / PARTS;
+  constexpr bool kWide = PARTS == 8;   // up to 128 segments: two (m, l) per lane
   __shared__ f32x4 partial[PARTS > 1 ? 8 : 1][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -119,9 +120,20 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
       m = v[0];
       l = v[1];
     }
-    M = wave_max(m);
+    // more than 64 segments (balanced caps up to 128): lane s also holds
+    // segment s + 64
+    float m2 = -__builtin_inff(), l2 = 0.f;
+    if constexpr (kWide) {
+      if (lane + 64 < S) {
+        const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + ((lane + 64) * rows_total + row) * 2));
+        m2 = v[0];
+        l2 = v[1];
+      }
+    }
+    M = wave_max(kWide ? fmaxf(m, m2) : m);
     const float coef = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * l;
-    den = wave_sum(coef);
+    const float coef2 = m2 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m2 - M) * l2;
+    den = wave_sum(kWide ? coef + coef2 : coef);
 
     for (int s0 = sb; s0 < se; s0 += kBatch) {
       if (s0 > sb) {
@@ -131,7 +143,11 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k)
-        if (s0 + k < se) num += lane_value(coef, s0 + k) * __builtin_convertvector(a[k], f32x4);
+        if (s0 + k < se) {
+          const int s = s0 + k;   // wave-uniform
+          const float c = kWide && s >= 64 ? lane_value(coef2, s - 64) : lane_value(coef, s & 63);
+          num += c * __builtin_convertvector(a[k], f32x4);
+        }
     }
   }
   if constexpr (PARTS > 1) {
@@ -175,10 +191,13 @@ hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<2, true>), grid, dim3(512), 0, stream, p);
     else hipLaunchKernelGGL((segment_reduce_kernel<2, false>), grid, dim3(512), 0, stream, p);
-  } else {
+  } else if (p.num_segments <= 64) {
     const dim3 grid((unsigned)((rows + 1) / 2));
     if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<4, true>), grid, dim3(512), 0, stream, p);
     else hipLaunchKernelGGL((segment_reduce_kernel<4, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    // above 64 segments (balanced caps only): eight waves per row
+    hipLaunchKernelGGL((segment_reduce_kernel<8, true>), dim3((unsigned)rows), dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }

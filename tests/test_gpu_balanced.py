@@ -25,13 +25,13 @@ def _gpu():
     pfkv.load_library()
 
 
-def _run(case, cap=64, **kw):
+def _run(case, cap=128, **kw):
     return pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                             case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale,
                             num_segments=cap, balance_segments=True, **kw)
 
 
-@pytest.mark.parametrize("cap", [64, 40, 17, 4, 2])
+@pytest.mark.parametrize("cap", [128, 100, 65, 64, 40, 17, 4, 2])
 def test_balanced_ragged_parity(cap):
     case = make_case(workload("ragged"), "cpu").to(DEV)
     print(f"[balanced] ragged cap={cap} ctx={case.workload.ctx}", flush=True)
@@ -112,7 +112,7 @@ def test_balanced_rerun_graph_and_short_rows_bitwise():
     ones = torch.tensor([0] + [1 if cu[b + 1] > cu[b] else 0 for b in range(len(cu) - 1)], dtype=torch.int32)
     cu1 = torch.cumsum(ones, 0).to(torch.int32).to(DEV)
     short = pfkv.verify_attn(q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, cu1,
-                             case.k_descale, case.v_descale, case.softmax_scale, num_segments=64,
+                             case.k_descale, case.v_descale, case.softmax_scale, num_segments=128,
                              balance_segments=True)
     torch.cuda.synchronize()
     assert torch.equal(short.view(torch.int16), base[torch.tensor(rows, device=DEV)].view(torch.int16))

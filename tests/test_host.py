@@ -93,6 +93,11 @@ CASES = [
     ("balanced, cap 1", dict(balance_segments=1, num_segments=1, workspace_size=pfkv.workspace_bytes(1, 64, 16)),
      "gfx950", INVALID),
     ("balance flag 2", dict(balance_segments=2), "gfx950", INVALID),
+    ("balanced, cap 128", dict(balance_segments=1, num_segments=128, workspace_size=pfkv.workspace_bytes(128, 64, 16)),
+     "gfx950", OK),
+    ("balanced, cap 129", dict(balance_segments=1, num_segments=129, workspace_size=pfkv.workspace_bytes(129, 64, 16)),
+     "gfx950", INVALID),
+    ("uniform, 65 segments", dict(num_segments=65, workspace_size=pfkv.workspace_bytes(65, 64, 16)), "gfx950", INVALID),
     ("max_q_len 8 too many queries", dict(max_q_len=8, total_q=129), "gfx950", INVALID),
     ("max_q_len 9", dict(max_q_len=9), "gfx950", INVALID),
     ("max_q_len negative", dict(max_q_len=-1), "gfx950", INVALID),
