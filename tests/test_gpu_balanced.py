@@ -116,3 +116,20 @@ def test_balanced_rerun_graph_and_short_rows_bitwise():
                              balance_segments=True)
     torch.cuda.synchronize()
     assert torch.equal(short.view(torch.int16), base[torch.tensor(rows, device=DEV)].view(torch.int16))
+
+
+@pytest.mark.parametrize("hq,hkv,max_q,page,head_dim", [(32, 2, 4, 16, 256), (16, 1, 8, 16, 256),
+                                                        (16, 1, 4, 1, 256), (8, 1, 4, 32, 128)])
+def test_balanced_other_shapes(hq, hkv, max_q, page, head_dim):
+    """Balanced segments with two work-groups per KV head (32 query heads),
+    two query-token blocks per sequence (up to 8 tokens), one-token and 32-token
+    pages, and head dim 128: the schedule's slots per work-group column change."""
+    q_lens = (max_q, 1, 3, max_q)
+    w = Workload(name="bs", ctx=(12000, 40, 700, 9), q_lens=q_lens, num_q_heads=hq, num_kv_heads=hkv,
+                 num_segments=None, seed=64 + hq + max_q + page, page_size=page, head_dim=head_dim,
+                 softmax_scale=1.0 / head_dim ** 0.5)
+    case = make_case(w, "cpu").to(DEV)
+    print(f"[balanced] hq={hq} hkv={hkv} max_q={max_q} page={page} d={head_dim}", flush=True)
+    out = _run(case, max_q_len=max_q)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), f"balanced hq={hq} max_q={max_q} page={page} d={head_dim}")
