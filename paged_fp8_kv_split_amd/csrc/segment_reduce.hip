@@ -16,7 +16,9 @@
 // One wave per output row, eight rows per work-group (measured 1 us faster per
 // call than four at 16 x 35000: fewer, fuller work-groups): lane s holds
 // (m_s, l_s), lane i dims 4i .. 4i + 3 of the fp16 o rows (head dim 128: lanes
-// 0-31), whose loads for up to 16 segments are in flight together.
+// 0-31), whose loads for up to 16 segments are in flight together. Above 16
+// segments 2, 4 or (balanced caps above 64) 8 waves share a row; BAL takes each
+// row's segment count from the balanced schedule instead of num_segments.
 #include "pfkv_internal.h"
 
 namespace pfkv {
@@ -69,6 +71,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // segments and few rows (4 sequences x 64 segments: 256 rows) one wave per
 // row would load its segments in several dependent batches on a few CUs.
 // PARTS = 1 is one wave per row, the segments summed in order s = 0, 1, ...
+// PARTS = 8 serves up to 128 segments: each lane then holds two (m, l) pairs.
 template <int PARTS, bool BAL>
 __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   constexpr int kRowsPerWg = 8 / PARTS;
