@@ -1166,6 +1166,21 @@ splitkv_main_kernel(MainParams p) {
   Geo geo;
   geo.seg = blockIdx.x;
   geo.b = blockIdx.y;
+  int wg_z = blockIdx.z;
+  if constexpr (!BAL) {
+    // Consecutive work-group ids are dispatched to the eight XCDs in turn.
+    // Renumber them so that each XCD runs a contiguous run of ids (a whole
+    // sequence's segments, when the grid allows): the sequence's queries and
+    // block-table row are then fetched into one XCD's L2, not into all eight.
+    const unsigned gx = gridDim.x, gxy = gx * gridDim.y, total = gxy * gridDim.z;
+    if ((total & 7u) == 0) {
+      const unsigned id = blockIdx.x + gx * (blockIdx.y + gridDim.y * blockIdx.z);
+      const unsigned r = (id & 7u) * (total >> 3) + (id >> 3);
+      geo.seg = (int)(r % gx);
+      geo.b = (int)((r / gx) % gridDim.y);
+      wg_z = (int)(r / gxy);
+    }
+  }
   // BAL: balanced segments (a separate instantiation, so that the default
   // kernel's code does not carry the schedule)
   int seg_count = p.num_segments;
@@ -1189,7 +1204,7 @@ splitkv_main_kernel(MainParams p) {
     }
     if (geo.b < 0) return;
   }
-  geo.h = blockIdx.z / p.q_split;
+  geo.h = wg_z / p.q_split;
   geo.hkv = geo.h / p.kv_split;
   // out-of-contract values are clamped so that every access stays in its buffer
   const int seq_q0 = cu[geo.b];
@@ -1197,7 +1212,7 @@ splitkv_main_kernel(MainParams p) {
   if (seq_q0 < 0 || seq_q0 >= p.total_q) seq_qlen = 0;
   seq_qlen = min(max(seq_qlen, 0), min(kMaxQLen, p.total_q - max(seq_q0, 0)));
   // this work-group's block of the sequence's query tokens
-  const int i0 = (blockIdx.z % p.q_split) * p.q_per_wg;
+  const int i0 = (wg_z % p.q_split) * p.q_per_wg;
   const int q_len = min(seq_qlen - i0, p.q_per_wg);
   if (q_len <= 0) return;
   geo.q0 = seq_q0 + i0;
