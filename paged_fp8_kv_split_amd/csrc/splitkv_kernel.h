@@ -25,11 +25,16 @@
 //   P.V waves accumulate step t - 2. A step's scores stay in registers across
 //   one barrier, so every score wave knows, before forming P, whether any of
 //   them saw a row pass its threshold (below).
-// * K/V pages move with global_load_lds_dwordx4 (1 KiB contiguous per
-//   instruction) issued from inline asm, so the compiler does not serialise LDS
-//   reads behind every outstanding transfer. K and V have rings of their own
-//   (4 stages each); each runs three steps ahead of its consumer, with explicit
-//   vmcnt waits. Page ids are staged in LDS windows by 4-byte LDS transfers.
+// * K and V take different paths to their LDS rings (4 stages each), so that
+//   the two kinds of read share the memory system: K pages move with
+//   global_load_lds_dwordx4 (1 KiB contiguous per instruction, HBM -> LDS with
+//   no registers) issued by the score waves from inline asm, three steps ahead
+//   of their use, with explicit vmcnt waits; V pages are read by the P.V waves
+//   with 16-byte vector loads into registers one phase before they go to LDS.
+//   On random 4 KiB pages vector loads alone stream about 6.9 TB/s, LDS DMA
+//   alone about 6.1 TB/s (and unevenly across the XCDs), a half-and-half mix
+//   about 6.8 TB/s; the mix also keeps the P.V waves' registers within budget.
+//   Page ids are staged in LDS windows by 4-byte LDS transfers.
 // * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K converts exactly from e4m3fn to
 //   bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1), Q stays bf16. The score layout
 //   puts one query row per lane column.
@@ -45,6 +50,9 @@
 // * P is rounded to fp16 once; the same values feed the row sum l and P V.
 // * O += P V on v_mfma_f32_16x16x32_f16. V's transposed operand comes from
 //   ds_read_b64_tr_b8 and converts exactly to fp16.
+// * Epilogue (16-bit arithmetic): o = O / l leaves the P.V waves' registers
+//   through a transpose inside groups of lanes (DPP swaps) and goes straight
+//   to memory, each row as runs of contiguous 8-byte stores.
 #pragma once
 
 #include <type_traits>
@@ -61,6 +69,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -259,7 +268,10 @@ struct PageStream {
   const uint8_t* cache;
   const int32_t* bt_row;      // this sequence's block-table row
   uint64_t page_stride;       // bytes between 16-token blocks (TOK: between tokens) of the cache
+  int pshift;                 // log2(page_stride) when it is a power of two, else -1
   unsigned goff[kParts];      // per-lane source offsets inside a block (TOK: inside a token's page)
+  unsigned lane_lds;          // vector transport: slot * block bytes + 16 lane (the LDS-DMA lane layout)
+  u32x4 buf[kParts];          // vector transport: the block in flight between load() and store()
   unsigned ring;              // LDS address of this slot in stage 0
   unsigned ids_lds;           // this wave's two page-id windows
   const int* ids;
@@ -276,6 +288,7 @@ struct PageStream {
     cache = cache_;
     bt_row = p.block_tables + (int64_t)geo.b * p.block_table_stride;
     page_stride = (uint64_t)(TOK ? 1 : kPageSize) * p.num_kv_heads * D;
+    pshift = (page_stride & (page_stride - 1)) == 0 ? __builtin_ctzll(page_stride) : -1;
     slot = slot_;
     pb = geo.pb;
     pe = geo.pe;
@@ -289,8 +302,10 @@ struct PageStream {
     for (int jj = 0; jj < kParts; ++jj) {
       const int k = Dm::kRowsPerKiB * jj + r;
       goff[jj] = (unsigned)(((TOK ? 0 : k * p.num_kv_heads) + geo.hkv) * D + 16 * (c ^ Dm::sw(k, jpar)));
+      buf[jj] = u32x4{0u, 0u, 0u, 0u};
     }
     ring = ring_stage0 + slot * Dm::kPageBytes;
+    lane_lds = (unsigned)(slot * Dm::kPageBytes + 16 * lane);
     ids_lds = lds_addr(smem + off_ids) + wave * (2 * 64 * 4);
     ids = (const int*)(smem + off_ids) + wave * (2 * 64);
     next_id = Ids{};
@@ -342,6 +357,11 @@ struct PageStream {
   __device__ int first_id(int t) const {            // scalar load, before the windows land
     return ((const const_i32*)bt_row)[(has(t) ? pb + kPagesPerStep * t + slot : pb) >> rlog];
   }
+  // first byte of 16-token block (TOK: token) blk >= 0: a shift where the stride
+  // is a power of two (one KV head: 4 KiB), a 64-bit product otherwise
+  __device__ const uint8_t* block_base(int blk) const {
+    return pshift >= 0 ? cache + ((uint64_t)(unsigned)blk << pshift) : cache + (uint64_t)(unsigned)blk * page_stride;
+  }
   // TOK: source of part jj (this lane's token R jj + r), its page clamped into the cache
   __device__ const uint8_t* token_src(const Ids& e, int jj) const {
     const int id = min(max((int)e[jj], 0), num_pages - 1);
@@ -353,30 +373,34 @@ struct PageStream {
 #pragma unroll
       for (int jj = 0; jj < kParts; ++jj) dma_1k_addr(token_src(entry, jj), dst + 1024 * jj);
     } else {
-      const uint8_t* base = cache + (uint64_t)resolve(t, entry) * page_stride;
+      const uint8_t* base = block_base(resolve(t, entry));
 #pragma unroll
       for (int jj = 0; jj < kParts; ++jj) dma_1k(base, goff[jj], dst + 1024 * jj);
     }
   }
   // The transfer of step t in kParts parts that the caller spreads over its
   // work: begin() resolves the page (and refills the window when due),
-  // part(q, jj) moves the jj-th KiB.
+  // part(q, jj) moves the jj-th KiB. FULL: the caller knows that step t
+  // exists and has this page slot (steady-state phases), so nothing is tested.
   struct Pending {
     const uint8_t* base;
     unsigned dst;
     bool on;
     Ids e;
   };
+  template <bool FULL = false>
   __device__ Pending begin(int t, int lane) {
-    Pending q{nullptr, 0u, has(t), Ids{}};
+    Pending q{nullptr, 0u, FULL || has(t), Ids{}};
     if (q.on) {
       refill(t, lane);
+      // one-token pages: the entries (four per lane) are read from their
+      // window here rather than a step ahead, to keep registers free
       if constexpr (TOK)
-        q.e = next_id;
+        q.e = read_id(t);
       else
-        q.base = cache + (uint64_t)resolve(t, __builtin_amdgcn_readfirstlane(next_id)) * page_stride;
+        q.base = block_base(resolve(t, __builtin_amdgcn_readfirstlane(next_id)));
       q.dst = ring + (t % kStages) * Dm::kStageBytes;
-      next_id = read_id(t + 1);
+      if constexpr (!TOK) next_id = read_id(t + 1);
     }
     return q;
   }
@@ -388,6 +412,29 @@ struct PageStream {
         dma_1k(q.base, goff[jj], q.dst + 1024 * jj);
     }
   }
+  // Vector transport: load() brings the block of step t (begin()'s pending
+  // transfer) into registers with 16-byte loads, lane i taking the 16 bytes
+  // that an LDS-DMA transfer would place at 16 i (the swizzle lives in the
+  // source offsets); store() writes them to the ring stage of step t. Between
+  // the two the block is in flight while the wave computes.
+  __device__ void load(const Pending& q, u32x4 (&dst)[kParts]) const {
+    if (q.on) {
+#pragma unroll
+      for (int jj = 0; jj < kParts; ++jj) {
+        if constexpr (TOK)
+          dst[jj] = __builtin_nontemporal_load((const u32x4*)token_src(q.e, jj));
+        else
+          dst[jj] = __builtin_nontemporal_load((const u32x4*)(q.base + goff[jj]));
+      }
+    }
+  }
+  __device__ void load(const Pending& q) { load(q, buf); }
+  __device__ void store(int t, uint8_t* ring_base, const u32x4 (&src)[kParts]) const {
+    uint8_t* dst = ring_base + lane_lds + (t % kStages) * Dm::kStageBytes;
+#pragma unroll
+    for (int jj = 0; jj < kParts; ++jj) *(u32x4*)(dst + 1024 * jj) = src[jj];
+  }
+  __device__ void store(int t, uint8_t* ring_base) const { store(t, ring_base, buf); }
 };
 
 // Stores the staged 16-bit rows ([row][D] in LDS) of the work-group, all
@@ -451,13 +498,14 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   const bool capped = p.softcap > 0.f;
   uint8_t* const k_ring = smem + C::kOffStage;
 
-  PageStream<TOK, D> ks;   // K of page slot w: streamed by P.V wave w + 4, read here
+  PageStream<TOK, D> ks;   // K of page slot w: streamed by LDS DMA and read here
   ks.init(p, geo, smem, w, w, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
 
   // ---- prologue. Q goes HBM -> LDS (V ring stages 2-3, not used before
   // phase 1) by page-style transfers, 16-byte chunk c of row r at position
-  // c ^ (r & 15), score wave w moving rows 16w..16w+15, while the P.V waves
-  // start the K and V streams. Q moves to registers after the first barrier.
+  // c ^ (r & 15), score wave w moving rows 16w..16w+15; then the K stream's
+  // first three steps, while the P.V waves start the V stream. Q moves to
+  // registers after the first barrier.
   constexpr int kQRow = Dm::kQRowBytes, kQRpk = Dm::kQRowsPerKiB, kQLanes = 64 / kQRpk;
   uint8_t* const q_stage = smem + C::kOffStage + (kStages + 2) * kStageBytes;
   if (n_steps > 0) {
@@ -472,7 +520,22 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         dma_1k(q_base, voff, lds_addr(q_stage) + (16 * w + kQRpk * k) * kQRow);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    ks.fetch_window(0, lane);
+    if constexpr (TOK) {
+      if (4 < n_steps) ks.fetch_window(1, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // one step's entries at a time (four per lane), to keep registers free
+      if (ks.has(0)) ks.put(0, ks.read_id(0));
+      if (ks.has(1)) ks.put(1, ks.read_id(1));
+      if (ks.has(2)) ks.put(2, ks.read_id(2));
+    } else {
+      const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
+      if (ks.has(0)) ks.put(0, id0);
+      if (ks.has(1)) ks.put(1, id1);
+      if (ks.has(2)) ks.put(2, id2);
+    }
+    wait_vm(ks.count(1) + ks.count(2));   // Q, the windows and K of step 0
+    ks.next_id = ks.read_id(3);
   }
   // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
   // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
@@ -557,11 +620,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 
   f32x4 sv[NRB];            // raw scores of the current step: lane (g, n) key 4g + r, row 16 rb + n
   float m_ref[NRB];         // reference max (log2 units) of row 16 rb + n, identical in every score wave
+  float m_off[NRB];         // m_ref, or 0 while it is -inf: P = 2^(s c2r - m_off)
   float thr[NRB];           // raw-score threshold (m + slack) / c2r
   float l_lane[NRB];        // this lane's share of the row sums
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     m_ref[rb] = -__builtin_inff();
+    m_off[rb] = 0.f;
     thr[rb] = -__builtin_inff();
     l_lane[rb] = 0.f;
   }
@@ -632,11 +697,9 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     f32x4 pv[NRB];
     auto exps = [&]() {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float mref = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2r[rb], -mref));
-      }
+        for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2r[rb], -m_off[rb]));
     };
     exps();
     if (__builtin_amdgcn_readfirstlane(flag_word) != 0) {
@@ -657,6 +720,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
           const float m_new = M * c2r[rb];
           alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);   // 0 when m was -inf
           m_ref[rb] = m_new;
+          m_off[rb] = m_new == -__builtin_inff() ? 0.f : m_new;
           thr[rb] = (m_new + kLazySlack) * inv_c2r[rb];
         }
         l_lane[rb] *= alpha;
@@ -679,9 +743,11 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const f16x4 ph = {(_Float16)pv[rb][0], (_Float16)pv[rb][1], (_Float16)pv[rb][2], (_Float16)pv[rb][3]};
-        *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = ph;
-        const f16x2 lo = {ph[0], ph[1]}, hi = {ph[2], ph[3]};
+        // the packed halves pass through an empty asm so that the compiler keeps
+        // them for the row sum instead of converting every value a second time
+        f16x2 lo = {(_Float16)pv[rb][0], (_Float16)pv[rb][1]}, hi = {(_Float16)pv[rb][2], (_Float16)pv[rb][3]};
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        *(f16x4*)(smem + p_off + pbuf * C::kPBytes + rb * (2 * 64 * 16)) = f16x4{lo[0], lo[1], hi[0], hi[1]};
         l_lane[rb] = __builtin_amdgcn_fdot2(hi, one, __builtin_amdgcn_fdot2(lo, one, l_lane[rb], false), false);
       }
     }
@@ -704,6 +770,11 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 #pragma unroll
       for (int u = 0; u < kKU; ++u) kraw[u] = *(const u32x4*)(smem + k_off[u] + kst * kStageBytes);
     }
+    {
+      const typename PageStream<TOK, D>::Pending kq = ks.template begin<!kTail>(t + 3, lane);
+#pragma unroll
+      for (int jj = 0; jj < PageStream<TOK, D>::kParts; ++jj) ks.part(kq, jj);
+    }
     if (have_p) form_p(t - 1, (kst + 3) & 1, flag_word);
     if (have_s) {
       if (kTail && (t + 2 >= n_steps || (t == 0 && win_head)))
@@ -713,12 +784,16 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       bool over = false;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) over |= sv[rb][r] > thr[rb];
+        over |= fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3])) > thr[rb];
       const bool any = __any(over);
       if (lane == 0) smem[C::kOffFlag + 4 * (kst & 1) + w] = any ? 1 : 0;
     }
-    lds_barrier();   // the P.V waves have waited for K of step t+1
+    // K of step t+1 must have landed; steps t+2 and t+3 may fly
+    if constexpr (kTail)
+      wait_vm(ks.count(t + 2) + ks.count(t + 3));
+    else
+      wait_vm(2 * PageStream<TOK, D>::kParts);
+    lds_barrier();
   };
 
   if (n_steps > 0) {
@@ -795,8 +870,10 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       }
     }
   }
-  lds_barrier();   // o staged
-  store_rows<G, D>(p, geo, smem + C::kOffObuf);
+  if constexpr (F8P) {
+    lds_barrier();   // o staged
+    store_rows<G, D>(p, geo, smem + C::kOffObuf);
+  }
 }
 
 // P.V wave v = w - 4: V stream of page slot v, O[:, 64 v .. 64 v + 63] for all
@@ -820,38 +897,24 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   uint8_t* const k_ring = smem + C::kOffStage;
   uint8_t* const v_ring = k_ring + kStages * kStageBytes;
 
-  // Both blocks of page slot v stream through this wave: K (page-id windows
-  // in the slot of score wave v, which streams nothing) three steps ahead of
-  // its use by the score waves, V three steps ahead of its use here.
-  PageStream<TOK, D> ks, vs;
-  ks.init(p, geo, smem, v, v, lane, p.k_cache, lds_addr(k_ring), C::kOffIds);
+  // The V block of page slot v streams through this wave by vector loads into
+  // registers, one phase before it goes to its ring stage and two before its
+  // use here.
+  PageStream<TOK, D> vs;
   vs.init(p, geo, smem, w, v, lane, p.v_cache, lds_addr(v_ring), C::kOffIds);
   if (n_steps > 0) {
-    ks.fetch_window(0, lane);
+    using Pend = typename PageStream<TOK, D>::Pending;
     vs.fetch_window(0, lane);
+    Pend v0;
     if constexpr (TOK) {
-      // one-token pages: the entries come from the windows (steps 0..3 in
-      // window 0; window 1, due at step 4, is fetched here too)
-      if (4 < n_steps) {
-        ks.fetch_window(1, lane);
-        vs.fetch_window(1, lane);
-      }
+      if (4 < n_steps) vs.fetch_window(1, lane);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      const auto id0 = ks.read_id(0), id1 = ks.read_id(1), id2 = ks.read_id(2);
-      if (ks.has(0)) ks.put(0, id0);
-      if (ks.has(1)) ks.put(1, id1);
-      if (ks.has(2)) ks.put(2, id2);
-      if (vs.has(0)) vs.put(0, id0);
-      wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // K of step 0
+      v0 = Pend{nullptr, 0u, vs.has(0), vs.read_id(0)};
     } else {
-      const int id0 = ks.first_id(0), id1 = ks.first_id(1), id2 = ks.first_id(2);
-      if (ks.has(0)) ks.put(0, id0);
-      if (ks.has(1)) ks.put(1, id1);
-      if (ks.has(2)) ks.put(2, id2);
-      if (vs.has(0)) vs.put(0, id0);
-      wait_vm(ks.count(1) + ks.count(2) + vs.count(0));   // the windows and K of step 0
+      v0 = Pend{vs.block_base(vs.resolve(0, vs.first_id(0))), 0u, vs.has(0), {}};
     }
-    ks.next_id = ks.read_id(3);
+    vs.load(v0);
+    wait_vm(vs.count(0));
     vs.next_id = vs.read_id(1);
   }
 
@@ -913,10 +976,10 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   bool slow1 = false;   // flag of step t-1 in phase t
   bool slow2 = false;   // flag of step t-2 in phase t
 
-  // Phase t: the LDS reads of step t-2 (V block, P) and of the flag word of
-  // step t-1 first; an extra barrier if step t-1 takes the slow path; the V
-  // transfer of step t+1; O += P V of step t-2 (rescaled first if step t-2
-  // moved m); wait for V of step t-1; barrier.
+  // Phase t: V of step t to its ring stage and the loads of V of step t+1;
+  // the LDS reads of step t-2 (V block, P) and of the flag word of step t-1;
+  // an extra barrier if step t-1 takes the slow path; O += P V of step t-2
+  // (rescaled first if step t-2 moved m); barrier.
   auto phase = [&](int t, auto tail, auto stage) {
     constexpr bool kTail = decltype(tail)::value;
     constexpr int kSt = decltype(stage)::value;
@@ -925,22 +988,15 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     const int u = t - 2;
     const int vst = kSt >= 0 ? ((kSt + 2) & 3) : (u & 3);
     const int pbuf = kSt >= 0 ? (kSt & 1) : (u & 1);
-    // K of step t+3 and V of step t+1: 2 kParts 1 KiB parts, spread over
-    // the MFMA groups below so that a part that waits for room in the memory
-    // pipeline does not hold up the whole phase's arithmetic
-    constexpr int kAll = 2 * kParts;
-    const typename PageStream<TOK, D>::Pending kq = ks.begin(t + 3, lane);
-    const typename PageStream<TOK, D>::Pending vq = vs.begin(t + 1, lane);
-    auto parts = [&](int d0, int d1) {
-      __builtin_amdgcn_sched_barrier(0);
-      for (int d = d0; d < d1; ++d) {
-        if (d < kParts)
-          ks.part(kq, d);
-        else
-          vs.part(vq, d - kParts);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
+    // V of step t (loaded in the previous phase) to its ring stage, then the
+    // loads of V of step t+1 go out; they land while this phase computes.
+    // Steady-state phases (t + 7 < n_steps) have every page slot of steps t
+    // and t + 1.
+    if (!kTail || vs.has(t)) vs.store(t, v_ring);
+    {
+      const typename PageStream<TOK, D>::Pending vq = vs.template begin<!kTail>(t + 1, lane);
+      vs.load(vq);
+    }
     unsigned flag_word = 0;
     if (have_f) flag_word = *(const unsigned*)(smem + C::kOffFlag + 4 * ((t - 1) & 1));
     // k-slot 8g + e of k-step kk is key 4g + (e & 3) of page slot 2 kk + (e >> 2)
@@ -998,6 +1054,17 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           }
         }
       }
+      i32x8 vb[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        vb[dt] = i32x8{vraw[dt][0][0], vraw[dt][0][1], vraw[dt][1][0], vraw[dt][1][1],
+                       vraw[dt][2][0], vraw[dt][2][1], vraw[dt][3][0], vraw[dt][3][1]};
+      auto accumulate = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
+      };
       if (slow2) {
         // rows 32 rt + 8 c + 4 (lane >> 5) + e hold acc8[rt][dt][4 c + e]
 #pragma unroll
@@ -1011,41 +1078,41 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
               for (int e = 0; e < 4; ++e) acc8[rt][dt][4 * c + e] *= a[e];
           }
       }
-      i32x8 vb[NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        vb[dt] = i32x8{vraw[dt][0][0], vraw[dt][0][1], vraw[dt][1][0], vraw[dt][1][1],
-                       vraw[dt][2][0], vraw[dt][2][1], vraw[dt][3][0], vraw[dt][3][1]};
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
-          const int gi = rt * NDT + dt;
-          parts(kAll * gi / (NDT * NRT), kAll * (gi + 1) / (NDT * NRT));
-        }
+      accumulate();
     } else if (!F8 && have_pv) {
-      f16x8 vf[2][NDB];
+      // V^T of k-step kk, converted exactly to fp16; keys of pages past the
+      // segment (never loaded: stale or uninitialised LDS) and past the
+      // sequence end get V = 0, so P = 0 never meets a NaN. Converted one
+      // k-step at a time, so that only half of the operands are live.
+      auto v_operands = [&](int kk, f16x8 (&vf)[NDB]) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vf[kk][db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
-      if constexpr (kTail) {
-        // keys of pages past the segment (never loaded: stale or uninitialised
-        // LDS) and past the sequence end get V = 0, so P = 0 never meets a NaN
-        if (u == n_steps - 1) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
+        for (int db = 0; db < NDB; ++db) vf[db] = fp8x8_to_f16((unsigned)vraw[kk][db][0], (unsigned)vraw[kk][db][1]);
+        if constexpr (kTail) {
+          if (u == n_steps - 1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int page = pb + kPagesPerStep * u + 2 * kk + (e >> 2);
               const int key = kPageSize * page + 4 * g + (e & 3);
               const bool keep = page < pe && key < L;
 #pragma unroll
-              for (int db = 0; db < NDB; ++db) vf[kk][db][e] = keep ? vf[kk][db][e] : (_Float16)0.f;
+              for (int db = 0; db < NDB; ++db) vf[db][e] = keep ? vf[db][e] : (_Float16)0.f;
             }
+          }
         }
-      }
+      };
+      auto accumulate = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          f16x8 vf[NDB];
+          v_operands(kk, vf);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[db], acc[rb][db], 0, 0, 0);
+          }
+        }
+      };
       if (slow2) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -1056,25 +1123,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
             for (int r = 0; r < 4; ++r) acc[rb][db][r] *= a[r];
         }
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][kk], vf[kk][db], acc[rb][db], 0, 0, 0);
-          const int gi = kk * NRB + rb;
-          parts(kAll * gi / (2 * NRB), kAll * (gi + 1) / (2 * NRB));
-        }
-    } else {
-      parts(0, kAll);
+      accumulate();
     }
-    // K of step t+1 and V of step t-1 (issued in phase t-2) must have landed;
-    // the transfers of phases t-1 and t may fly
-    if constexpr (kTail)
-      wait_vm(ks.count(t + 2) + vs.count(t) + ks.count(t + 3) + vs.count(t + 1));
-    else
-      wait_vm(4 * kParts);
     lds_barrier();
   };
 
@@ -1118,32 +1168,79 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
           }
         }
       }
+    lds_barrier();
+    store_rows<G, D>(p, geo, smem + C::kOffObuf);
   } else {
+    // o = acc / l (0 with no visible key); a single segment writes out = vd o.
+    // Lane (g, n) holds dims kVDims v + 16 db + n of rows 16 rb + 4 g + r. A
+    // transpose inside each group of NDB lanes (butterflies over the lane
+    // index on packed 16-bit pairs) leaves lane n = NDB q + j with the NDB
+    // consecutive dims kVDims v + 16 j + NDB q + e, which it stores with one
+    // write: no staging through LDS, and the 16 lanes of a row write one
+    // contiguous run.
+    const int j = n & (NDB - 1), q = n / NDB;
+    const int dim0 = kVDims * v + 16 * j + NDB * q;
+    const bool odd = (n & 1) != 0, half = ((n >> 1) & 1) != 0;
+    const unsigned sel = odd ? 0x03020706u : 0x05040100u;   // (partner.hi, own.hi) : (own.lo, partner.lo)
+    auto epilogue = [&](auto direct_tag) {
+      constexpr bool kDirect = decltype(direct_tag)::value;
+      const int T = p.total_q, Hq = p.num_q_heads;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * rb + 4 * g + r;
-      if (row < rows) {
-        float l = lsum[row];
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rb + 4 * g + r;
+          float l = lsum[row];
 #pragma unroll
-        for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
-        if (p.direct && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
-        // o = acc / l (0 with no visible key); a single segment writes out = vd o
-        const float inv = l > 0.f ? vd / l : 0.f;
+          for (int s2 = 1; s2 < kPagesPerStep; ++s2) l += lsum[s2 * C::kRows + row];
+          if (kDirect && p.sinks != nullptr) l += lsum[kPagesPerStep * C::kRows + row];
+          const float inv = l > 0.f ? vd * __builtin_amdgcn_rcpf(l) : 0.f;
+          unsigned wd[NDB / 2];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int at = row * D + kVDims * v + 16 * db + n;
-          if (p.direct)
-            obuf_bits[at] = (uint16_t)bf16_rne(acc[rb][db][r] * inv);
-          else
-            obuf[at] = (_Float16)(acc[rb][db][r] * inv);
+          for (int k = 0; k < NDB / 2; ++k) {
+            const float a = acc[rb][2 * k][r] * inv, b = acc[rb][2 * k + 1][r] * inv;
+            if constexpr (kDirect) {
+              wd[k] = bf16_rne(a) | (bf16_rne(b) << 16);
+            } else {
+              const f16x2 hv = {(_Float16)a, (_Float16)b};
+              wd[k] = __builtin_bit_cast(unsigned, hv);
+            }
+          }
+          if constexpr (NDB == 4) {
+            // lanes n and n ^ 2 trade the pair whose bit 1 differs from theirs
+            const unsigned t0 = (unsigned)__builtin_amdgcn_mov_dpp((int)wd[0], 0x4E, 0xF, 0xF, false);
+            const unsigned t1 = (unsigned)__builtin_amdgcn_mov_dpp((int)wd[1], 0x4E, 0xF, 0xF, false);
+            const unsigned w0 = half ? t1 : wd[0], w1 = half ? wd[1] : t0;
+            wd[0] = w0;
+            wd[1] = w1;
+          }
+          // lanes n and n ^ 1 trade the 16-bit half whose bit differs from theirs
+#pragma unroll
+          for (int k = 0; k < NDB / 2; ++k)
+            wd[k] = __builtin_amdgcn_perm((unsigned)__builtin_amdgcn_mov_dpp((int)wd[k], 0xB1, 0xF, 0xF, false), wd[k], sel);
+          if (row < rows) {
+            const int i = row / G, gg = row - (row / G) * G;
+            if constexpr (kDirect) {
+              uint16_t* dst = p.out + (int64_t)(q0 + i) * p.out_stride_token + (int64_t)(h * G + gg) * p.out_stride_head + dim0;
+              if constexpr (NDB == 4)
+                *(uint2*)dst = make_uint2(wd[0], wd[1]);
+              else
+                *(unsigned*)dst = wd[0];
+            } else {
+              uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + dim0;
+              if constexpr (NDB == 4)
+                __builtin_nontemporal_store(u32x2{wd[0], wd[1]}, (u32x2*)dst);
+              else
+                __builtin_nontemporal_store(wd[0], (unsigned*)dst);
+            }
+          }
         }
-      }
-    }
+    };
+    if (p.direct)
+      epilogue(std::true_type{});
+    else
+      epilogue(std::false_type{});
   }
-  lds_barrier();
-  store_rows<G, D>(p, geo, smem + C::kOffObuf);
 }
 
 template <int G, int NRB, int MODE, bool TOK, int D>
