@@ -39,8 +39,12 @@ PAGES_PREFILL_US = {"prefill_12k": 2158.0}
 # The pages' gfx950 assembly kernel + reduce on this workload: 67 us per call,
 # i.e. 286.72 MB / 67 us = 4.28 TB/s under the same bytes / time formula.
 PAGES_TBPS = 286.72e6 / 67e-6 / 1e12
-# calls per timing round for the median-of-rounds figure
-ROUND = 64
+# the timed region is split into this many rounds (by events, no syncs) for
+# the median-of-rounds figure
+N_ROUNDS = 4
+# every timed region is preceded by at least this much wall time of the same
+# calls, so that clocks are steady (aiter PR #7375, Performance: 1 s warmup)
+WARMUP_SECONDS = 1.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "splitkv_main_prod_counters.json")
 # precision name -> (C ABI value, dtype text)
 PRECISIONS = {
@@ -52,6 +56,21 @@ PRECISIONS = {
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def warm_up(fn, min_calls, torch, seconds=WARMUP_SECONDS):
+    """Run fn(k) for k = 0, 1, ... until at least min_calls calls and `seconds`
+    of wall time have passed (checked every 16 calls, after a sync); returns the
+    number of calls."""
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        fn(k)
+        k += 1
+        if k % 16 == 0 or k >= min_calls:
+            torch.cuda.synchronize()
+            if k >= min_calls and time.perf_counter() - t0 >= seconds:
+                return k
 
 
 def kernel_source_digest():
@@ -75,20 +94,23 @@ def measured_traffic(workload_name):
 
 
 def stream_ceiling(pfkv, torch, gib=4, reps=5):
-    """Best-of-reps read rate (TB/s) of the three streaming-read variants."""
+    """Best-of-reps read rate (TB/s) of the four streaming-read variants over a
+    4 GiB buffer (the ordered ones visit its 4 KiB blocks in a random order)."""
     nbytes = gib << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     order = torch.randperm(nbytes // 4096, device="cuda").to(torch.int32)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = {}
-    for variant, name in ((0, "contiguous_vector"), (1, "contiguous_lds_dma"), (2, "random_page_lds_dma")):
-        pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None, sink=sink)
+    for variant, name in ((0, "contiguous_vector"), (1, "contiguous_lds_dma"), (2, "random_page_lds_dma"),
+                          (3, "random_page_vector")):
+        ordered = order if variant in (2, 3) else None
+        pfkv.stream_read(buf, variant, page_order=ordered, sink=sink)
         torch.cuda.synchronize()
         best = float("inf")
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None, sink=sink)
+            pfkv.stream_read(buf, variant, page_order=ordered, sink=sink)
             e1.record()
             torch.cuda.synchronize()
             best = min(best, e0.elapsed_time(e1) * 1e-3)
@@ -309,49 +331,60 @@ def main():
         if st != 0:
             raise binding.PfkvError(st, binding.last_error())
 
-    for k in range(args.warmup):
-        call(k)
-    torch.cuda.synchronize()
+    warm_calls = warm_up(call, args.warmup, torch)
 
     # ---- timed region: exactly --steps calls
-    # Extra events every ROUND calls split the same region into rounds (no sync
-    # between them), for the median-of-rounds figure beside the whole-region mean.
+    # Events at N_ROUNDS evenly spaced points split the same region into rounds
+    # (no sync between them), for the median-of-rounds figure beside the mean.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_rounds = min(N_ROUNDS, args.steps)
+    cuts = {args.steps * r // n_rounds for r in range(1, n_rounds)}
     marks = []
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     ev0.record(stream)
     for k in range(args.steps):
         call(k)
-        if (k + 1) % ROUND == 0 and k + 1 < args.steps:
-            marks.append(torch.cuda.Event(enable_timing=True))
-            marks[-1].record(stream)
+        if k + 1 in cuts:
+            marks.append((k + 1, torch.cuda.Event(enable_timing=True)))
+            marks[-1][1].record(stream)
     ev1.record(stream)
     host_s = time.perf_counter() - h0
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     us_per_call = total_ms * 1e3 / args.steps
     tbps = w.kv_bytes / (us_per_call * 1e-6) / 1e12
-    bounds = [ev0] + marks + ([ev1] if args.steps % ROUND == 0 else [])
-    rounds_us = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 / ROUND for i in range(len(bounds) - 1)]
-    median_round_us = statistics.median(rounds_us) if rounds_us else None
-    log(f"{args.steps} calls: {us_per_call:.2f} us/call, {tbps:.3f} TB/s effective "
+    bounds = [(0, ev0)] + marks + [(args.steps, ev1)]
+    rounds_us = [bounds[i][1].elapsed_time(bounds[i + 1][1]) * 1e3 / (bounds[i + 1][0] - bounds[i][0])
+                 for i in range(len(bounds) - 1)]
+    median_round_us = statistics.median(rounds_us)
+    log(f"{warm_calls} warmup calls, then {args.steps} calls: {us_per_call:.2f} us/call, {tbps:.3f} TB/s effective "
         f"(host {host_s * 1e6 / args.steps:.1f} us/call to enqueue); "
-        f"{len(rounds_us)} rounds of {ROUND}: median {median_round_us} us/call")
+        f"{len(rounds_us)} rounds: median {median_round_us:.2f} us/call")
 
     # ---- main kernel alone: the same number of back-to-back main-kernel
     # launches (same replica rotation) between two events on the launch stream
-    for k in range(min(args.warmup, 20)):
-        lib.pfkv_splitkv_main(refs[k % R], handle)
-    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    m0.record(stream)
-    for k in range(args.steps):
-        st = lib.pfkv_splitkv_main(refs[k % R], handle)
-        if st != 0:
-            raise binding.PfkvError(st, binding.last_error())
-    m1.record(stream)
-    torch.cuda.synchronize()
-    main_us = m0.elapsed_time(m1) * 1e3 / args.steps
+    def main_alone():
+        warm_up(lambda k: lib.pfkv_splitkv_main(refs[k % R], handle), args.warmup, torch)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for k in range(args.steps):
+            st = lib.pfkv_splitkv_main(refs[k % R], handle)
+            if st != 0:
+                raise binding.PfkvError(st, binding.last_error())
+        m1.record(stream)
+        torch.cuda.synchronize()
+        return m0.elapsed_time(m1) * 1e3 / args.steps
+
+    main_us = main_alone()
+    # the main kernel alone must not take longer than the whole call (main +
+    # reduce); if it does, the clocks moved between the two regions: measure
+    # the main kernel once more
+    consistent = main_us <= us_per_call
+    if not consistent:
+        log(f"main kernel alone ({main_us:.2f} us) above the whole call ({us_per_call:.2f} us): measuring again")
+        main_us = main_alone()
+        consistent = main_us <= us_per_call
     achieved_gbps = w.kv_bytes / (main_us * 1e-6) / 1e9
     log(f"main kernel alone: {main_us:.2f} us/launch, {achieved_gbps / 1e3:.3f} TB/s")
 
@@ -373,9 +406,7 @@ def main():
             if st != 0:
                 raise binding.PfkvError(st, binding.last_error())
     replays = max(1, -(-args.steps // R))
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
+    warm_up(lambda k: graph.replay(), 2, torch)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
     for _ in range(replays):
@@ -393,8 +424,7 @@ def main():
         if other_name == args.precision:
             continue
         argv_o, refs_o = make_refs(other)
-        for k in range(args.warmup):
-            lib.pfkv_verify_attn_fwd(refs_o[k % R], handle)
+        warm_up(lambda k: lib.pfkv_verify_attn_fwd(refs_o[k % R], handle), args.warmup, torch)
         v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         v0.record(stream)
         for k in range(args.steps):
@@ -470,6 +500,7 @@ def main():
             "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "main_kernel_us": round(main_us, 2),
+            "main_kernel_us_le_call": bool(consistent),
         },
         "ceiling_TBps": ceiling,
         "frac_of_measured_ceiling": round(tbps / best_ceiling, 4) if best_ceiling else None,

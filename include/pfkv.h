@@ -227,13 +227,21 @@ int pfkv_device_info(int device, char* arch, int arch_len, int* num_cus);
 /*
  * Streaming-read microbenchmark kernels (aiter PR #5190, Microbenchmark: a
  * streaming-read microbenchmark that bounds the achievable read rate). Reads
- * `bytes` bytes of `buf` once and writes a checksum word to `sink` (4 bytes of
- * device memory) so the reads cannot be elided.
- *   variant 0: contiguous 16-byte vector loads into registers, grid-stride;
- *   variant 1: contiguous 4 KiB pages through LDS with global_load_lds_dwordx4;
- *   variant 2: as 1, visiting pages in the order given by page_order
- *              (num_pages int32 page indices in [0, bytes / 4096)).
- * bytes must be a positive multiple of 4096 for variants 1 and 2 and of 16 for 0.
+ * `bytes` bytes of `buf` once, as 4 KiB blocks, with one work-group of 8 waves
+ * per CU:
+ *   variant 0: blocks in address order, 16-byte vector loads into registers;
+ *   variant 1: blocks in address order through LDS with global_load_lds_dwordx4
+ *              (each block read back from LDS);
+ *   variant 2: as 1, visiting blocks in the order given by page_order
+ *              (num_pages int32 block indices in [0, bytes / 4096); out-of-range
+ *              entries are clamped);
+ *   variant 3: as 0, in the order given by page_order.
+ * Every 32-bit word read is XORed into the 4-byte device word `sink` (atomic
+ * XOR, not cleared here): with sink zeroed first and page_order a permutation
+ * of all blocks, sink ends as the XOR of the whole buffer, which proves that
+ * every byte was read. bytes must be a positive multiple of 4096, buf 16-byte
+ * aligned, sink 4-byte aligned; all pointers device memory of the current
+ * device. Enqueues one kernel on `stream`; returns a pfkv_status.
  */
 int pfkv_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t* page_order,
                      int64_t num_pages, void* sink, void* stream);

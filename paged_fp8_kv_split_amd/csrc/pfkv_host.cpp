@@ -431,17 +431,18 @@ int pfkv_stream_read(const void* buf, uint64_t bytes, int variant, const int32_t
                      void* sink, void* stream) {
   g_last_error.clear();
   if (buf == nullptr || sink == nullptr) return fail(PFKV_INVALID, "buf and sink must be non-NULL");
-  if (variant < 0 || variant > 2) return fail(PFKV_INVALID, "variant must be 0, 1 or 2");
-  if (bytes == 0 || bytes % (variant == 0 ? 16 : 4096)) return fail(PFKV_INVALID, "bad byte count for variant");
+  if (variant < 0 || variant > 3) return fail(PFKV_INVALID, "variant must be 0, 1, 2 or 3");
+  if (bytes == 0 || bytes % 4096) return fail(PFKV_INVALID, "bytes must be a positive multiple of 4096");
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(PFKV_INVALID, "buf must be 16-byte aligned");
-  if (variant == 2 && (page_order == nullptr || num_pages < 1))
-    return fail(PFKV_INVALID, "variant 2 needs a page order");
+  const bool ordered = variant == 2 || variant == 3;
+  if (ordered && (page_order == nullptr || num_pages < 1))
+    return fail(PFKV_INVALID, "variants 2 and 3 need a page order");
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e == hipSuccess) {
     int st = check_device_pointer(buf, device, "buf");
     if (st == PFKV_OK) st = check_device_pointer(sink, device, "sink");
-    if (st == PFKV_OK && variant == 2) st = check_device_pointer(page_order, device, "page_order");
+    if (st == PFKV_OK && ordered) st = check_device_pointer(page_order, device, "page_order");
     if (st != PFKV_OK) return st;
     e = pfkv::launch_stream_read(buf, bytes, variant, page_order, num_pages, (uint32_t*)sink,
                                  (hipStream_t)stream);

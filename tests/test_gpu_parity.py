@@ -335,9 +335,19 @@ def test_host_pointer_is_refused():
                          case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, num_segments=4)
 
 
-def test_stream_read_variants_run():
-    buf = torch.ones(64 << 20, dtype=torch.uint8, device=DEV)
-    order = torch.randperm((64 << 20) // 4096, device=DEV).to(torch.int32)
-    for variant in (0, 1, 2):
-        pfkv.stream_read(buf, variant, page_order=order if variant == 2 else None)
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_stream_read_reads_every_byte(variant):
+    """Each streaming-read variant folds every 32-bit word it reads into the sink
+    by XOR; over a 64 MiB buffer of random words (a random block order for the
+    ordered variants) that must equal the XOR of the whole buffer, computed on
+    the host: a variant that skipped or repeated a block would not match."""
+    nbytes = 64 << 20
+    g = torch.Generator().manual_seed(77 + variant)
+    host = torch.randint(0, 1 << 31, (nbytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    buf = host.to(DEV).view(torch.uint8)
+    order = torch.randperm(nbytes // 4096, generator=g).to(torch.int32).to(DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pfkv.stream_read(buf, variant, page_order=order if variant in (2, 3) else None, sink=sink)
     torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == want

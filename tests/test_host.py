@@ -182,9 +182,14 @@ def test_workspace_bytes(lib):
 
 def test_stream_read_validation(lib):
     assert lib.pfkv_stream_read(None, 4096, 0, None, 0, None, None) == INVALID
-    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, 3, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
-    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 100, 1, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
-    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, 2, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, 4, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, -1, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    for variant in (0, 1, 2, 3):
+        # whole 4 KiB blocks only
+        assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 100, variant, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
+    for variant in (2, 3):
+        # the ordered variants need a page order
+        assert lib.pfkv_stream_read(ctypes.c_void_p(0x1000), 4096, variant, None, 0, ctypes.c_void_p(0x2000), None) == INVALID
 
 
 def test_python_wrapper_needs_gpu_tensors():
