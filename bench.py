@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup-seconds", type=float, default=WARMUP_SECONDS,
+                    help="minimum wall time of warmup calls before each timed region")
     ap.add_argument("--workload", default="prod")
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--segments", type=int, default=None)
@@ -331,7 +333,7 @@ def main():
         if st != 0:
             raise binding.PfkvError(st, binding.last_error())
 
-    warm_calls = warm_up(call, args.warmup, torch)
+    warm_calls = warm_up(call, args.warmup, torch, args.warmup_seconds)
 
     # ---- timed region: exactly --steps calls
     # Events at N_ROUNDS evenly spaced points split the same region into rounds
@@ -365,7 +367,7 @@ def main():
     # ---- main kernel alone: the same number of back-to-back main-kernel
     # launches (same replica rotation) between two events on the launch stream
     def main_alone():
-        warm_up(lambda k: lib.pfkv_splitkv_main(refs[k % R], handle), args.warmup, torch)
+        warm_up(lambda k: lib.pfkv_splitkv_main(refs[k % R], handle), args.warmup, torch, args.warmup_seconds)
         m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         m0.record(stream)
         for k in range(args.steps):
@@ -406,7 +408,7 @@ def main():
             if st != 0:
                 raise binding.PfkvError(st, binding.last_error())
     replays = max(1, -(-args.steps // R))
-    warm_up(lambda k: graph.replay(), 2, torch)
+    warm_up(lambda k: graph.replay(), 2, torch, args.warmup_seconds)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
     for _ in range(replays):
@@ -424,7 +426,7 @@ def main():
         if other_name == args.precision:
             continue
         argv_o, refs_o = make_refs(other)
-        warm_up(lambda k: lib.pfkv_verify_attn_fwd(refs_o[k % R], handle), args.warmup, torch)
+        warm_up(lambda k: lib.pfkv_verify_attn_fwd(refs_o[k % R], handle), args.warmup, torch, args.warmup_seconds)
         v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         v0.record(stream)
         for k in range(args.steps):

@@ -149,21 +149,28 @@ typedef struct pfkv_args {
 enum pfkv_precision { PFKV_PRECISION_16BIT = 0, PFKV_PRECISION_FP8_P = 1, PFKV_PRECISION_FP8 = 2 };
 
 /*
- * Pure host-side validation; reads no device memory and needs no GPU.
+ * Pure host-side validation; reads no device memory and needs no GPU. It is the
+ * argument check of the launcher that aiter PR #5190 describes (Modifications:
+ * the C++ launcher validates its arguments before the two launches; Supported:
+ * what is outside the supported set is rejected by a check).
  * arch: the device's gcnArchName (e.g. "gfx950:sramecc+:xnack-"); anything not
  * starting with "gfx950" is PFKV_UNSUPPORTED. num_cus: compute units (> 0).
  * Returns a pfkv_status; on failure pfkv_last_error() says which check failed.
  * Device-side preconditions that are NOT checked here (they would need a device
- * read): 0 <= n_b <= 4, n_b <= L_b <= page_size * max_pages_per_seq, and block
- * table entries in [0, num_pages). The kernels clamp each of them so that no
- * access leaves its buffer; results for inputs that break them are unspecified.
+ * read): 0 <= n_b <= max_q_len (4 when max_q_len is 0), n_b <= L_b <=
+ * page_size * max_pages_per_seq, and block table entries in [0, num_pages).
+ * The kernels clamp each of them so that no access leaves its buffer; results
+ * for inputs that break them are unspecified.
  */
 int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
 
 /*
  * Enqueue the verify-attention call on `stream` (a hipStream_t; NULL = the null
  * stream): the split-KV main kernel on a grid of num_segments x num_seqs x
- * num_kv_heads work-groups (x 2 when G = 32), then the segment reduce. With num_segments == 1
+ * (num_kv_heads * kv_split * q_split) work-groups, kv_split = 2 when G = 32 (two
+ * work-groups of 16 query heads per KV head) and q_split = 2 when 16 query heads
+ * per work-group meet max_q_len > 4 (two blocks of at most 4 query tokens),
+ * each 1 otherwise; then the segment reduce. With num_segments == 1
  * the main kernel writes out itself and no reduce is enqueued (the workspace is
  * still validated but not touched). Validates with
  * pfkv_check_args against the current device first and checks that the device
@@ -206,8 +213,9 @@ int pfkv_segment_reduce(const pfkv_args* args, void* stream);
 int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
 
 /*
- * Workspace bytes for S segments: S * total_q * num_q_heads * 520. 0 for bad
- * sizes. Layout (after the main kernel): fp16 o[S][total_q][num_q_heads][256],
+ * Workspace bytes for S segments (aiter PR #5190, Modifications: the Python
+ * entry point allocates the split-KV workspaces the launcher writes and the
+ * reduce reads): S * total_q * num_q_heads * 520. 0 for bad sizes. Layout (after the main kernel): fp16 o[S][total_q][num_q_heads][256],
  * the segment's softmax-weighted mean of V (without v_descale, 0 for a segment
  * with no visible key; at head_dim 128 the first 128 of each row), then fp32 (m, l)[S][total_q][num_q_heads], m the
  * segment's reference max of the scores in log2 units (-inf when empty) and
@@ -215,7 +223,11 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
  */
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads);
 
-/* Text of the most recent failure on this host thread ("" if none). Valid until the next call. */
+/*
+ * Text of the most recent failure on this host thread ("" if none), naming the
+ * check that failed (aiter PR #5190, Supported: unsupported inputs are rejected
+ * by a check rather than run). Valid until the next call on the thread.
+ */
 const char* pfkv_last_error(void);
 
 /*

@@ -1269,8 +1269,11 @@ splitkv_main_kernel(MainParams p) {
     // Renumber them so that each XCD runs a contiguous run of ids (a whole
     // sequence's segments, when the grid allows): the sequence's queries and
     // block-table row are then fetched into one XCD's L2, not into all eight.
-    const unsigned gx = gridDim.x, gxy = gx * gridDim.y, total = gxy * gridDim.z;
-    if ((total & 7u) == 0) {
+    // The renumbering is a bijection of [0, total) only while its 32-bit
+    // arithmetic is exact: grids of 2^32 work-groups or more keep their ids.
+    const uint64_t total64 = (uint64_t)gridDim.x * gridDim.y * gridDim.z;
+    if ((total64 & 7u) == 0 && total64 <= 0xffffffffull) {
+      const unsigned gx = gridDim.x, gxy = gx * gridDim.y, total = (unsigned)total64;
       const unsigned id = blockIdx.x + gx * (blockIdx.y + gridDim.y * blockIdx.z);
       const unsigned r = (id & 7u) * (total >> 3) + (id >> 3);
       geo.seg = (int)(r % gx);

@@ -99,17 +99,14 @@ def test_fp8_long_segments_parity(mode, segments):
 
 @mode_param
 @pytest.mark.parametrize("name", ["prod", "gqa8"])
-def test_fp8_full_size_sampled(mode, name):
+def test_fp8_full_size_all_rows(mode, name):
     prec, bounds = MODES[mode]
     w = workload(name)
     case = make_case(w, DEV)
     out = run(case, num_segments=w.num_segments, precision=prec)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    seqs = [0, w.num_seqs - 1]
-    ref = oracle_for(subset(case, seqs))
-    got = out[torch.tensor(rows_of(case, seqs), device=DEV)]
-    assert_parity(got, ref, f"{mode} {name} seqs {seqs}", bounds)
+    ref = oracle_for(subset(case, list(range(w.num_seqs))))
+    assert_parity(out, ref, f"{mode} {name}, all {w.num_seqs} sequences", bounds)
 
 
 @mode_param
@@ -171,7 +168,8 @@ def test_fp8_dominant_key_flushes_small_probabilities(mode):
     """The fp8-P underflow the aiter PR #7375 review works through: with one key
     scoring 7 and 3999 keys scoring 0, P = e^-7 ~ 9e-4 of the maximum is below half
     the smallest e4m3 subnormal (2^-10) and flushes to zero, so the output is V of
-    the dominant key (+1) instead of the exact -0.8745 the 16-bit path returns."""
+    the dominant key (+1) instead of the exact (e^7 - 3999) / (e^7 + 3999) =
+    -0.5696 the 16-bit path returns."""
     from test_gpu_parity import _code, _one_sequence
     n = 4000
     k = np.zeros((n, 1, 256), np.uint8)
