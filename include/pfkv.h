@@ -193,6 +193,21 @@ int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);
 int pfkv_set_debug(int on);
 
 /*
+ * pfkv_verify_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same validation, kernels and results, but the per-segment partials go to a
+ * device array the library holds (PFKV_NOALLOC_SCRATCH_BYTES bytes on each GPU it
+ * runs on, until the process ends) instead of args->workspace, which is ignored
+ * (it may be NULL, workspace_size 0). A call whose partials need more
+ * (pfkv_workspace_bytes(num_segments, total_q, num_q_heads) > the limit) returns
+ * PFKV_INVALID. It calls no allocating routine and does not run the debug check.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race; serialize them.
+ */
+#define PFKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int pfkv_verify_attn_fwd_noalloc(const pfkv_args* args, void* stream);
+
+/*
  * The two stages of pfkv_verify_attn_fwd, exposed separately (same arguments,
  * same validation) so that a caller can place or time them individually:
  * pfkv_splitkv_main enqueues only the split-KV main kernel, which writes the

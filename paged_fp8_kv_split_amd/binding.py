@@ -127,6 +127,8 @@ def load_library():
     lib.pfkv_check_args.restype = ctypes.c_int
     lib.pfkv_verify_attn_fwd.argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
     lib.pfkv_verify_attn_fwd.restype = ctypes.c_int
+    lib.pfkv_verify_attn_fwd_noalloc.argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
+    lib.pfkv_verify_attn_fwd_noalloc.restype = ctypes.c_int
     for name in ("pfkv_splitkv_main", "pfkv_segment_reduce"):
         getattr(lib, name).argtypes = [ctypes.POINTER(PfkvArgs), ctypes.c_void_p]
         getattr(lib, name).restype = ctypes.c_int
@@ -211,6 +213,7 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
 
     ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device,
     ``sinks`` (optional) a contiguous float32 ``[Hq]`` tensor on q's device.
+    ``workspace`` may be None (pointer NULL, size 0) for the allocation-free call.
     """
     k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
@@ -238,9 +241,11 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
                     ("seq_lens", seq_lens), ("cu_seqlens_q", cu_seqlens_q), ("out", out),
                     ("workspace", workspace)):
+        if t is None:
+            continue
         if t.device != q.device:
             raise ValueError(f"{name} must be on q's device ({q.device}), got {t.device}")
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
         raise TypeError("workspace must be a contiguous uint8 tensor")
     if lse is not None:
         if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
@@ -252,11 +257,12 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.block_tables, a.seq_lens, a.cu_seqlens_q = (block_tables.data_ptr(), seq_lens.data_ptr(),
                                                   cu_seqlens_q.data_ptr())
     a.k_descale, a.v_descale = k_descale.data_ptr(), v_descale.data_ptr()
-    a.workspace, a.out = workspace.data_ptr(), out.data_ptr()
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.out = out.data_ptr()
     a.q_stride_token, a.q_stride_head = q.stride(0), q.stride(1)
     a.out_stride_token, a.out_stride_head = out.stride(0), out.stride(1)
     a.block_table_stride = block_tables.stride(0)
-    a.workspace_size = workspace.numel()
+    a.workspace_size = workspace.numel() if workspace is not None else 0
     a.num_seqs = seq_lens.numel()
     a.total_q = q.shape[0]
     a.num_q_heads = q.shape[1]
@@ -327,6 +333,26 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     _raise_on(lib.pfkv_verify_attn_fwd(ctypes.byref(a), ctypes.c_void_p(handle)))
+    return (out, lse) if lse is not None else out
+
+
+def verify_attn_noalloc(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
+                        softmax_scale, num_segments, out, stream=None, precision=PRECISION_16BIT, lse=None,
+                        sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=False):
+    """The allocation-free call (``pfkv_verify_attn_fwd_noalloc``): the caller
+    passes ``out`` (and ``lse`` if wanted) and an explicit ``num_segments``;
+    the partials go to the library's own device array, so neither this wrapper
+    nor the library allocates. Calls that overlap on one GPU race."""
+    lib = load_library()
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
+                   softmax_scale, num_segments, out, None, precision, lse, sinks, window_left, softcap,
+                   max_q_len, balance_segments)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _raise_on(lib.pfkv_verify_attn_fwd_noalloc(ctypes.byref(a), ctypes.c_void_p(handle)))
     return (out, lse) if lse is not None else out
 
 

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libpfkv.so")
 
 KERNEL_SOURCES = ["splitkv_main.hip", "splitkv_main_fp8p.hip", "splitkv_main_fp8.hip", "splitkv_main_hd128.hip",
                   "segment_reduce.hip",
-                  "stream_read.hip", "debug_check.hip", "prefill.hip"]
+                  "stream_read.hip", "debug_check.hip", "prefill.hip", "noalloc.hip"]
 SOURCES = ["pfkv_host.cpp", *KERNEL_SOURCES]
 # headers the kernel sources include (a change to one rebuilds everything anyway)
 HEADERS = ["pfkv_internal.h", "splitkv_kernel.h"]

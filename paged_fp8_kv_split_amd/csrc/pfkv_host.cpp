@@ -258,8 +258,10 @@ int pfkv_device_info(int device, char* arch, int arch_len, int* num_cus) {
 
 namespace {
 
-// Validation shared by the three launch entry points; fills the kernel params.
-int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
+// Validation shared by the launch entry points; fills the kernel params.
+// library_workspace: the workspace is the library's own device array (the
+// allocation-free entry point), which is not memory HIP's pointer query knows.
+int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bool library_workspace = false) {
   g_last_error.clear();
   int device = 0;
   hipError_t e = hipGetDevice(&device);
@@ -277,6 +279,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp) {
       {a->seq_lens, "seq_lens"}, {a->cu_seqlens_q, "cu_seqlens_q"}, {a->k_descale, "k_descale"},
       {a->v_descale, "v_descale"}, {a->workspace, "workspace"}, {a->out, "out"}};
   for (const auto& x : ptrs) {
+    if (library_workspace && x.p == a->workspace) continue;
     st = check_device_pointer(x.p, device, x.name);
     if (st != PFKV_OK) return st;
   }
@@ -390,6 +393,28 @@ int launch_reduce(const pfkv::ReduceParams& rp, void* stream) {
 }
 
 }  // namespace
+
+namespace pfkv {
+
+// The verify call on a workspace the library owns (ws, ws_bytes): the same
+// validation and launches as pfkv_verify_attn_fwd, without the debug check
+// (which allocates and synchronizes).
+int verify_attn_library_workspace(const pfkv_args* a, void* ws, uint64_t ws_bytes, void* stream) {
+  if (a == nullptr) return fail(PFKV_INVALID, "args is NULL");
+  pfkv_args b = *a;
+  b.workspace = ws;
+  b.workspace_size = ws_bytes;
+  pfkv::MainParams mp;
+  pfkv::ReduceParams rp;
+  int st = prepare(&b, &mp, &rp, /*library_workspace=*/true);
+  if (st == PFKV_OK) st = launch_main(mp, b.num_q_heads / b.num_kv_heads, stream);
+  if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);
+  return st;
+}
+
+int set_error(int status, const char* msg) { return fail(status, msg); }
+
+}  // namespace pfkv
 
 extern "C" {
 

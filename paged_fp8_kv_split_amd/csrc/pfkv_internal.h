@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct pfkv_args;   // include/pfkv.h
+
 namespace pfkv {
 
 constexpr int kHeadDim = 256;   // largest head_dim served (also 128); the workspace row stride
@@ -145,6 +147,10 @@ struct CheckParams {
 };
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream);
+// The verify call of pfkv.h on a workspace the library owns (pfkv_host.cpp),
+// and the setter of the thread's last-error text.
+int verify_attn_library_workspace(const ::pfkv_args* a, void* ws, uint64_t ws_bytes, void* stream);
+int set_error(int status, const char* msg);
 // the e4m3-P and e4m3-Q/P modes at head dim 256, and every mode at head dim
 // 128, one translation unit each
 hipError_t launch_splitkv_main_fp8p(const MainParams& p, int group, hipStream_t stream);

@@ -133,3 +133,24 @@ def test_balanced_other_shapes(hq, hkv, max_q, page, head_dim):
     out = _run(case, max_q_len=max_q)
     torch.cuda.synchronize()
     assert_parity(out, oracle_for(case), f"balanced hq={hq} max_q={max_q} page={page} d={head_dim}")
+
+
+@pytest.mark.parametrize("balanced", [False, True])
+def test_stale_workspace_does_not_leak(balanced):
+    """Every partial the reduce reads is written by the main kernel of the same
+    call (empty segments write neutral records): a workspace full of 0xFF bytes
+    (fp16 NaN) gives the same bits as a zeroed one."""
+    case = make_case(workload("ragged"), "cpu").to(DEV)
+    segs = 128 if balanced else 40
+    need = pfkv.workspace_bytes(segs, case.q.shape[0], case.q.shape[1])
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                                     case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale,
+                                     num_segments=segs, workspace=ws, balance_segments=balanced,
+                                     return_lse=True))
+    torch.cuda.synchronize()
+    (o0, l0), (o1, l1) = outs
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
