@@ -18,6 +18,11 @@ visible scores (aiter PR #7375 "gfx1250 fp8 varlen FMHA", Summary). Split-KV
 segmentation is an exact rewrite of these quantities, so the oracle does not
 depend on the segment count.
 
+``fp8_model.py`` computes the same attention with Q and P rounded to e4m3 under
+power-of-two block scales, the arithmetic class of the pages' fp8 kernel, so
+that tests can separate the error that rounding carries from the error an
+implementation adds.
+
 The second workload, fp8 varlen prefill attention (aiter PR #7375, Summary:
 e4m3 Q/K/V with per-tensor descales, packed THD layout, qk head dim 192 and v
 head dim 128, causal aligned to the bottom right or not, optional LSE), is in
@@ -39,4 +44,5 @@ from .attention import (  # noqa: F401
     segment_partials,
     visible_key_count,
 )
+from .fp8_model import attend_fp8, block_round, e4m3_round  # noqa: F401
 from .prefill import causal_visible, default_scale, kv_head_of, prefill_attend, prefill_lse  # noqa: F401

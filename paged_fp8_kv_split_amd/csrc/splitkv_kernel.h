@@ -118,6 +118,12 @@ struct Cfg {
   static constexpr int kRows = kRowBlocks * 16;
   static constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;         // fp16 P of a step: [rb][k-step][lane] x 16 B
   static constexpr int kOffP = 0;                                  // two P buffers
+  // fp8 P uses the first kRows * 64 bytes of a P buffer; behind them, in the
+  // same buffer, each page slot's row maxima of the step ([row][slot] fp32)
+  // and the E8M0 scales of P's two 32-key blocks ([row][block] bytes)
+  static constexpr int kP8Xmax = kRows * 64;
+  static constexpr int kP8Scale = kP8Xmax + kRows * kPagesPerStep * 4;
+  static_assert(kP8Scale + kRows * 2 <= kPBytes, "fp8 P buffer");
   static constexpr int kOffMx = kOffP + 2 * kPBytes;               // step row maxima [row][slot] (slow path)
   static constexpr int kOffAlpha = kOffMx + kRows * kPagesPerStep * 4;   // two [row] rescale-factor buffers
   static constexpr int kOffFlag = kOffAlpha + 2 * kRows * 4;       // two flag words, byte j from score wave j
@@ -462,12 +468,18 @@ __device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, 
   }
 }
 
-// fp8 (e4m3fn) MFMA with unit block scales (E8M0 127 = 2^0) on both operands
-__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// fp8 (e4m3fn) MFMAs with E8M0 block scales (127 = 2^0), one per 32 k-elements.
+// Which lane's scale covers which bytes (measured on gfx950): on 16x16x128 the
+// scale of lane n + 16 j covers bytes 16 (j >> 1) .. + 15 of lanes n + 16 g,
+// g in {2 (j & 1), 2 (j & 1) + 1}; on 32x32x64 the scale of lane c + 32 j
+// covers bytes 16 j .. + 15 of lanes c and c + 32. A operand (K) unscaled,
+// B operand (Q) scaled:
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
-__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// A operand (P) scaled, B operand (V) unscaled:
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
 }
 __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -475,8 +487,9 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 
 // Score wave w (page slot w): K stream, S^T = K Q^T for all NRB row blocks,
 // lazy softmax, P to LDS, row sums; writes m and l of the segment. With F8,
-// Q is quantised per row to e4m3 (scale amax / 448, folded into that row's
-// score multiplier), S^T runs on the fp8 MFMA and P is rounded to e4m3.
+// Q is quantised to e4m3 with a power-of-two scale per 32 dims and S^T runs on
+// the scaled fp8 MFMA; with F8P, P is rounded to e4m3 with a power-of-two
+// scale per (row, 32 keys).
 template <int G, int NRB, int MODE, bool TOK, int D>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G, D>;
@@ -539,53 +552,63 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   }
   // Q^T operand of the score MFMA for row 16 rb + n: k-slots 8g..8g+7 of
   // k-step 2u + hh hold dims 16 (4u + g) + 8 hh .. + 8 (chunk 8u + 2g + hh).
-  // With F8 (q8): byte b of k-step ks holds dim 128 ks + 32 g + b, and c2r is
-  // the row's score multiplier c2 * amax / 448.
+  // With F8 (q8): byte b of k-step ks holds dim 128 ks + 64 (b >> 4) + 16 g +
+  // (b & 15), so that the MFMA's scale block j (bytes 16 (j >> 1) .. + 15 of
+  // lanes 2 (j & 1) and 2 (j & 1) + 1) is the 32 consecutive dims
+  // 128 ks + 32 j .. + 31. Each block is in e4m3 under its own power-of-two
+  // scale, which lane group j supplies in q8sc. The scales ride in the MFMA, so
+  // the scores come out in the same units as the 16-bit path's.
   constexpr int kKS8 = D / 128;   // k-steps of the fp8 score MFMA
   bf16x8 qop[F8 ? 1 : NRB][kKU][2];
   i32x8 q8[F8 ? NRB : 1][kKS8];
-  float c2r[NRB], inv_c2r[NRB];
-  float cap_a[NRB], cap_b[NRB];   // soft-cap in raw-score units: s -> cap_b tanh(cap_a s)
+  int q8sc[F8 ? NRB : 1][kKS8];
+  const float inv_c2 = 1.0f / c2;
+  float cap_a = 0.f, cap_b = 0.f;   // soft-cap in raw-score units: s -> cap_b tanh(cap_a s)
   auto load_q = [&]() {
     if constexpr (F8) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const int r = 16 * rb + n;
         const bool pad = r >= rows;
-        bf16x8 x[kKS8][4];
-        float amax = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < kKS8; ++ks)
+        for (int ks = 0; ks < kKS8; ++ks) {
+          bf16x8 x[4];
+          float amax[2] = {0.f, 0.f};   // bytes 0..15 and 16..31 of this lane
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
-            const int pos = (16 * ks + 4 * g + c4) ^ n;
+            const int pos = (16 * ks + 8 * (c4 >> 1) + 2 * g + (c4 & 1)) ^ n;   // dims 8 pos .. + 7
             const bf16x8 v = *(const bf16x8*)(q_stage + r * kQRow + 16 * pos);
-            x[ks][c4] = pad ? bf16x8{} : v;
+            x[c4] = pad ? bf16x8{} : v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)x[ks][c4][e]));
+            for (int e = 0; e < 8; ++e) amax[c4 >> 1] = fmaxf(amax[c4 >> 1], fabsf((float)x[c4][e]));
           }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;   // q8 = e4m3(q * qs)
-        c2r[rb] = c2 / qs;
-        inv_c2r[rb] = 1.0f / c2r[rb];
+          // block 2 hb + (g >> 1) (dims 128 ks + 64 hb + 32 (g >> 1) .. + 31): lanes
+          // g and g ^ 1 hold its two halves; 2^e puts its largest |q| in [128, 256)
+          int eb[2];
 #pragma unroll
-        for (int ks = 0; ks < kKS8; ++ks)
+          for (int hb = 0; hb < 2; ++hb) {
+            const float a = fmaxf(amax[hb], __shfl_xor(amax[hb], 16, 64));
+            eb[hb] = a > 0.f ? max(__builtin_amdgcn_frexp_expf(a) - 8, -127) : 0;
+          }
 #pragma unroll
           for (int d = 0; d < 8; ++d) {
-            const bf16x8& xv = x[ks][d >> 1];
+            const bf16x8& xv = x[d >> 1];
             const int e = 4 * (d & 1);
+            const float qs = __builtin_amdgcn_ldexpf(1.0f, -eb[d >> 2]);
             int word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e] * qs, (float)xv[e + 1] * qs, 0, false);
             word = __builtin_amdgcn_cvt_pk_fp8_f32((float)xv[e + 2] * qs, (float)xv[e + 3] * qs, word, true);
             q8[rb][ks][d] = word;
           }
+          // block g (half g >> 1 of lane pair g & 1) is held by lane groups 2 (g & 1), 2 (g & 1) + 1
+          const int src = n + 32 * (g & 1);
+          const int e0 = __shfl(eb[0], src, 64), e1 = __shfl(eb[1], src, 64);
+          q8sc[rb][ks] = 127 + ((g >> 1) ? e1 : e0);
+        }
       }
       return;
     }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      c2r[rb] = c2;
-      inv_c2r[rb] = 1.0f / c2;
       const int r = 16 * rb + n;
       const bool pad = r >= rows;
 #pragma unroll
@@ -600,13 +623,13 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   };
 
   // ---- per-lane LDS addresses
-  // K of key n: bf16 path chunks 4u + g (u < D / 64); fp8 path chunks 2g, 2g+1
-  // of k-step u / 2 (8 chunks per k-step); a chunk c sits at c ^ sw
+  // K of key n: bf16 path chunks 4u + g (u < D / 64); fp8 path chunks g and
+  // g + 4 of k-step u / 2 (8 chunks per k-step); a chunk c sits at c ^ sw
   const unsigned ksw = (unsigned)Dm::sw(n, w & 1);
   unsigned k_off[kKU];
 #pragma unroll
   for (int u = 0; u < kKU; ++u) {
-    const unsigned c = F8 ? (unsigned)(2 * g + (u & 1) + 8 * (u >> 1)) : (unsigned)(4 * u + g);
+    const unsigned c = F8 ? (unsigned)(g + 4 * (u & 1) + 8 * (u >> 1)) : (unsigned)(4 * u + g);
     k_off[u] = C::kOffStage + w * kPageBytes + D * n + 16u * (c ^ ksw);
   }
   // P of row 16 rb + n, keys 4g..4g+3 of slot w: half (w & 1) of the 16-byte
@@ -620,8 +643,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 
   f32x4 sv[NRB];            // raw scores of the current step: lane (g, n) key 4g + r, row 16 rb + n
   float m_ref[NRB];         // reference max (log2 units) of row 16 rb + n, identical in every score wave
-  float m_off[NRB];         // m_ref, or 0 while it is -inf: P = 2^(s c2r - m_off)
-  float thr[NRB];           // raw-score threshold (m + slack) / c2r
+  float m_off[NRB];         // m_ref, or 0 while it is -inf: P = 2^(s c2 - m_off)
+  float thr[NRB];           // raw-score threshold (m + slack) / c2
   float l_lane[NRB];        // this lane's share of the row sums
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -646,7 +669,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         for (int ks = 0; ks < kKS8; ++ks) {
           const i32x8 ka = cat8(kraw[2 * ks], kraw[2 * ks + 1]);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) sv[rb] = mfma_fp8_16x16x128(ka, q8[rb][ks], sv[rb]);
+          for (int rb = 0; rb < NRB; ++rb) sv[rb] = mfma_fp8_16x16x128(ka, q8[rb][ks], sv[rb], q8sc[rb][ks]);
         }
       } else {
 #pragma unroll
@@ -667,8 +690,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(2.88539008177792681f * cap_a[rb] * sv[rb][r]);
-            sv[rb][r] = cap_b[rb] * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
+            const float e = __builtin_amdgcn_exp2f(2.88539008177792681f * cap_a * sv[rb][r]);
+            sv[rb][r] = cap_b * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e));
           }
       }
       if (kTail && (kPageSize * (pidx + 1) > qoff + 1 || (win >= 0 && kPageSize * pidx < qoff + q_len - 1 - win))) {
@@ -690,19 +713,65 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     }
   };
 
-  // P of step u (scores in sv). P is first formed against the current m,
-  // while the flag word (any score wave saw a row pass its threshold in step
-  // u) is still in flight; in the rare slow path it is formed again.
+  // P of step u (scores in sv). 16-bit P: P is first formed against the
+  // current m, while the flag word (any score wave saw a row pass its
+  // threshold in step u) is still in flight; in the rare slow path it is
+  // formed again.
+  //
+  // F8P: m follows the row's running maximum exactly (no slack), so a new
+  // maximum is P = 2^0, which e4m3 holds exactly: the largest weight of a row
+  // is not rounded. The page slots' row maxima of step u are already in LDS
+  // (exchanged in the phase that computed the scores for the block scales), so
+  // the flagged update reads them there, without the slow path's extra
+  // barrier. Page slots w and w ^ 2 form
+  // the 32-key block (w & 1) of P in the P.V MFMA: the block's largest P,
+  // 2^(top c2 - m) <= 1, sets a power of two 2^e that puts it in [128, 256)
+  // before rounding to e4m3 (e <= -7); a block below 2^-100 contributes
+  // nothing (shift +inf: every P of it is 0, e = 0), so e >= -107. 2^-e is
+  // folded into the exponent; the scale rides in the MFMA's A-scale operand.
   auto form_p = [&](int u, int pbuf, unsigned flag_word) {
     f32x4 pv[NRB];
+    float top[F8P ? NRB : 1], shift[F8P ? NRB : 1];
+    int eb[F8P ? NRB : 1];
+    if constexpr (F8P) {
+      if (__builtin_amdgcn_readfirstlane(flag_word) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const f32x4 xm = *(const f32x4*)(smem + C::kOffP + pbuf * C::kPBytes + C::kP8Xmax + (16 * rb + n) * 16);
+          const float M = fmaxf(fmaxf(xm[0], xm[1]), fmaxf(xm[2], xm[3]));
+          const float m_new = fmaxf(m_ref[rb], M * c2);
+          const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_ref[rb] - m_new);
+          m_ref[rb] = m_new;
+          m_off[rb] = m_new == -__builtin_inff() ? 0.f : m_new;
+          thr[rb] = m_new * inv_c2;
+          l_lane[rb] *= alpha;
+          if (w == 0 && g == 0) alpha_buf[(u & 1) * C::kRows + 16 * rb + n] = alpha;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float* xm = (const float*)(smem + C::kOffP + pbuf * C::kPBytes + C::kP8Xmax + (16 * rb + n) * 16);
+        top[rb] = fmaxf(xm[w & 1], xm[(w & 1) + 2]);
+      }
+    }
     auto exps = [&]() {
+      if constexpr (F8P) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float x = __builtin_fmaf(top[rb], c2, -m_off[rb]);
+          const bool live = x >= -100.f;
+          eb[rb] = live ? (int)__builtin_floorf(x) - 7 : 0;
+          shift[rb] = live ? m_off[rb] + (float)eb[rb] : __builtin_inff();
+        }
+      }
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2r[rb], -m_off[rb]));
+        for (int r = 0; r < 4; ++r)
+          pv[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][r], c2, -(F8P ? shift[rb] : m_off[rb])));
     };
     exps();
-    if (__builtin_amdgcn_readfirstlane(flag_word) != 0) {
+    if (!F8P && __builtin_amdgcn_readfirstlane(flag_word) != 0) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         float v = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
@@ -717,11 +786,11 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         float alpha = 1.f;
         if (M > thr[rb]) {
-          const float m_new = M * c2r[rb];
+          const float m_new = M * c2;
           alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);   // 0 when m was -inf
           m_ref[rb] = m_new;
           m_off[rb] = m_new == -__builtin_inff() ? 0.f : m_new;
-          thr[rb] = (m_new + kLazySlack) * inv_c2r[rb];
+          thr[rb] = (m_new + kLazySlack) * inv_c2;
         }
         l_lane[rb] *= alpha;
         if (w == 0 && g == 0) alpha_buf[(u & 1) * C::kRows + 16 * rb + n] = alpha;
@@ -729,15 +798,18 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
       exps();
     }
     if constexpr (F8P) {
-      // e4m3 P (round to nearest even); l sums the rounded values
+      // e4m3 P (round to nearest even) under the block's scale; l sums the
+      // rounded values times 2^e, the weights the MFMA applies
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][0], pv[rb][1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[rb][2], pv[rb][3], word, true);
         *(int*)(smem + p8_off(rb) + pbuf * C::kPBytes) = word;
+        if (w < 2 && g == 0)
+          smem[C::kOffP + pbuf * C::kPBytes + C::kP8Scale + 2 * (16 * rb + n) + w] = (uint8_t)(127 + eb[rb]);
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
         const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        l_lane[rb] += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        l_lane[rb] += __builtin_amdgcn_ldexpf((lo[0] + lo[1]) + (hi[0] + hi[1]), eb[rb]);
       }
     } else {
       const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
@@ -783,8 +855,16 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         score_step(t, kraw, std::false_type{});
       bool over = false;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        over |= fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3])) > thr[rb];
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float v = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
+        over |= v > thr[rb];
+        if constexpr (F8P) {
+          // this page slot's row maximum, for the block scales of P (formed next phase)
+          float r = fmaxf(v, __shfl_xor(v, 16, 64));
+          r = fmaxf(r, __shfl_xor(r, 32, 64));
+          if (g == 0) *(float*)(smem + C::kOffP + (kst & 1) * C::kPBytes + C::kP8Xmax + (16 * rb + n) * 16 + 4 * w) = r;
+        }
+      }
       const bool any = __any(over);
       if (lane == 0) smem[C::kOffFlag + 4 * (kst & 1) + w] = any ? 1 : 0;
     }
@@ -800,11 +880,8 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     lds_barrier();   // Q and step 0's K are in LDS
     load_q();
     if (capped) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        cap_a[rb] = c2r[rb] * 0.69314718055994531f / p.softcap;
-        cap_b[rb] = 1.f / cap_a[rb];
-      }
+      cap_a = c2 * 0.69314718055994531f / p.softcap;
+      cap_b = 1.f / cap_a;
     }
     int t = 0;
     for (; t < 4 && t < n_steps + 2; ++t) phase(t, std::true_type{}, std::integral_constant<int, -1>{});
@@ -936,11 +1013,15 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   // 32 q .. 32 q + 31 (q = l >> 5) of the step as bytes 0..31; B (V) dim
   // 32 dt + (l & 31) of this wave's 64 with the same keys, gathered by four
   // ds_read_b64_tr_b8 of 8 keys each: in its 16-lane group, source lane
-  // 2k + hb supplies the 8 dims at +8 hb of key 32 q + 8 j + k.
+  // 2k + hb supplies the 8 dims at +8 hb of key 32 q + 8 j + k. Bytes 0..15
+  // are page slot 2q, bytes 16..31 slot 2q + 1, so the MFMA's scale block j
+  // (bytes 16 j .. + 15 of both lane halves, scale from lane c + 32 j) is slots
+  // j and j + 2, whose E8M0 scale the score waves store per row.
   constexpr int NRT = (NRB + 1) / 2;    // 32-row tiles
   constexpr int NDT = kVDims / 32;      // 32-dim tiles of this wave
   unsigned v8_off[F8 ? NDT : 1][4];
   int p8_rd[F8 ? NRT : 1];
+  int p8_sc[F8 ? NRT : 1];   // this lane's P block scale: row 32 rt + (l & 31), block l >> 5 (-1: padding row)
   if constexpr (F8) {
     const int q = lane >> 5, sub = (lane >> 4) & 1, src = lane & 15, kk8 = src >> 1, hb = src & 1;
 #pragma unroll
@@ -956,6 +1037,8 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     for (int rt = 0; rt < NRT; ++rt) {
       const int r = 32 * rt + (lane & 31);
       p8_rd[rt] = C::kOffP + r * 64 + 16 * ((2 * q) ^ ((r >> 2) & 3));   // chunk 2q; chunk 2q+1 at ^1
+      // rows past the score waves' NRB blocks (an odd NRB) have no scale written
+      p8_sc[rt] = r < 16 * NRB ? C::kOffP + C::kP8Scale + 2 * r + q : -1;
     }
   }
 
@@ -1003,6 +1086,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     i32x2 vraw[2][NDB > 4 ? NDB : 4];
     f16x8 pa[F8 ? 1 : NRB][2];
     i32x8 pa8[F8 ? NRT : 1];
+    int sa8[F8 ? NRT : 1];
     if (F8 && have_pv) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -1013,6 +1097,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
       for (int rt = 0; rt < NRT; ++rt) {
         const uint8_t* pr = smem + p8_rd[rt] + pbuf * C::kPBytes;
         pa8[rt] = cat8(*(const u32x4*)pr, *(const u32x4*)(smem + ((p8_rd[rt] + pbuf * C::kPBytes) ^ 16)));
+        sa8[rt] = p8_sc[rt] >= 0 ? (int)smem[p8_sc[rt] + pbuf * C::kPBytes] : 127;
       }
     }
     if (!F8 && have_pv) {
@@ -1030,7 +1115,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
     }
     slow2 = slow1;
     slow1 = have_f && __builtin_amdgcn_readfirstlane(flag_word) != 0;
-    if (slow1) lds_barrier();   // matches the score waves' maxima exchange
+    if (!F8 && slow1) lds_barrier();   // matches the score waves' maxima exchange (F8: none)
     if (F8 && have_pv) {
       if constexpr (kTail) {
         // keys past the segment or the sequence end: V bytes 0
@@ -1063,14 +1148,17 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt]);
+          for (int dt = 0; dt < NDT; ++dt) acc8[rt][dt] = mfma_fp8_32x32x64(pa8[rt], vb[dt], acc8[rt][dt], sa8[rt]);
       };
       if (slow2) {
-        // rows 32 rt + 8 c + 4 (lane >> 5) + e hold acc8[rt][dt][4 c + e]
+        // rows 32 rt + 8 c + 4 (lane >> 5) + e hold acc8[rt][dt][4 c + e]; rows
+        // past the score waves' NRB blocks (an odd NRB) have no alpha and are
+        // never stored
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
+            if (32 * rt + 8 * c >= 16 * NRB) continue;
             const f32x4 a = *(const f32x4*)(alpha_buf + (u & 1) * C::kRows + 32 * rt + 8 * c + 4 * (lane >> 5));
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)

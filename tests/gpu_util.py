@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle import fp8_model
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Case
 
@@ -13,6 +14,11 @@ MAX_ERR_SIGMA = 0.15
 MEAN_ERR_SIGMA = 0.02
 FP8_MAX_ERR_SIGMA = 0.15
 FP8_MEAN_ERR_SIGMA = 0.03
+# Where e4m3 rounding by itself (the fp64 model oracle.fp8_model on the same
+# input, in FP8_MODEL_REALIZATIONS roundings) exceeds the fp8 bar, a kernel is
+# held to the worst of the model's realizations times FP8_MODEL_SLACK instead.
+FP8_MODEL_REALIZATIONS = 4
+FP8_MODEL_SLACK = 1.1
 
 
 def run(case: Case, num_segments=None, out=None, workspace=None, precision=0):
@@ -71,3 +77,45 @@ def oracle_for(case: Case) -> np.ndarray:
 def rows_of(case: Case, seqs):
     cu = case.cu_seqlens_q.cpu().numpy()
     return [t for b in seqs for t in range(int(cu[b]), int(cu[b + 1]))]
+
+
+def _stats64(a: np.ndarray, ref: np.ndarray):
+    sigma = ref.std()
+    err = np.abs(a - ref)
+    return err.max() / sigma, err.mean() / sigma
+
+
+def assert_fp8_parity(got, case: Case, precision: int, label="", **opts):
+    """The fp8 bar (max 0.15 sigma, mean 0.03 sigma of the exact oracle output).
+
+    The fp64 model of the same roundings (e4m3 P under a power-of-two scale per
+    32 keys; with precision 2 also e4m3 Q under one per 32 dims) is evaluated on
+    the same input in a few equally valid realizations: the exact row maximum as
+    the reference P is taken against, and seeded per-row offsets of it (which
+    way each P rounds depends on that reference). Where every realization is
+    within the bar the kernel must be too; where one is above it (e4m3 keeps 3
+    mantissa bits, and some inputs carry more than 0.15 sigma from that alone)
+    the kernel is held to FP8_MODEL_SLACK times the worst realization, and the
+    case is reported as such. ``opts`` are the oracle options (window_left,
+    softcap, sinks as numpy)."""
+    arrs = case.to("cpu").host_arrays()
+    exact = oracle.attend(**arrs, **opts)
+    T, H = exact.shape[:2]
+    fmx, fmean = 0.0, 0.0
+    for k in range(FP8_MODEL_REALIZATIONS):
+        offsets = None if k == 0 else np.random.default_rng(k).uniform(0.0, 1.0, (T, H))
+        model = fp8_model.attend_fp8(**arrs, quantize_q=(precision == 2), p_offsets=offsets, **opts)
+        a, b = _stats64(model, exact)
+        fmx, fmean = max(fmx, a), max(fmean, b)
+    mx, mean = error_stats(got, exact)
+    within = fmx <= FP8_MAX_ERR_SIGMA and fmean <= FP8_MEAN_ERR_SIGMA
+    if within:
+        max_s, mean_s = FP8_MAX_ERR_SIGMA, FP8_MEAN_ERR_SIGMA
+    else:
+        max_s = max(FP8_MAX_ERR_SIGMA, FP8_MODEL_SLACK * fmx)
+        mean_s = max(FP8_MEAN_ERR_SIGMA, FP8_MODEL_SLACK * fmean)
+    print(f"[fp8 parity] {label}: max|err|/std={mx:.4f} mean|err|/std={mean:.5f}; e4m3 model (worst of "
+          f"{FP8_MODEL_REALIZATIONS}) {fmx:.4f} / {fmean:.5f} -> bar "
+          f"{'0.15/0.03' if within else 'model'} ({max_s:.3f}/{mean_s:.4f})", flush=True)
+    assert mx <= max_s and mean <= mean_s, (label, mx, mean, fmx, fmean)
+    return mx, mean, within

@@ -1,16 +1,17 @@
 """The fp8 variants of the main kernel against the CPU oracle.
 
-PFKV_PRECISION_FP8_P keeps the default scores and rounds P to e4m3 for an fp8
-P V. PFKV_PRECISION_FP8 also quantises each query row to e4m3 (scale
-amax / 448): the pages' precision class (aiter PR #5190, Kernel notes and
-Accuracy: 0.075-0.13 sigma). On these synthetic inputs both stay within the
-fp8 bar's mean (0.03 sigma) but exceed its max of 0.15 sigma: e4m3 P alone
-reaches 0.16-0.18 sigma, e4m3 Q and P 0.15-0.30 sigma. Each is therefore held
-to the band measured here (fp8 P: max 0.25, mean 0.03; fp8 Q/P: max 0.35,
-mean 0.035), and reading A of the small configuration (near-one-hot softmax,
-where e4m3 Q flips close maxima, 2.2 sigma) is left out for fp8 Q/P. The
-bit-exactness invariants of the default path hold for both, since Q is
-quantised per row. Every call goes through the C ABI.
+PFKV_PRECISION_FP8_P keeps the default scores and rounds P to e4m3 under a
+power-of-two scale per (row, 32 keys) for an fp8 P V; PFKV_PRECISION_FP8 also
+rounds Q to e4m3 under a power-of-two scale per 32 dims: the pages' precision
+class (aiter PR #5190, Kernel notes and Accuracy: 0.075-0.13 sigma). Every
+case is held to the fp8 bar (max 0.15 sigma, mean 0.03 sigma of the exact
+output) unless the fp64 model of the same roundings (oracle.fp8_model) is
+itself above it on that input; then the kernel is held to 1.2 times the
+model's error (gpu_util.assert_fp8_parity). On these N(0, 1) inputs e4m3 Q
+alone carries 0.13-0.30 sigma, so fp8 Q/P cases mostly take the second form,
+and the near-one-hot softmax of reading A (where e4m3 Q flips close maxima)
+about 2.2 sigma. The bit-exactness invariants of the default path hold for both,
+since Q is quantised within its own row. Every call goes through the C ABI.
 """
 
 import math
@@ -19,16 +20,16 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Workload, make_case, permute_pool, workload
 
-from gpu_util import FP8_MEAN_ERR_SIGMA, assert_parity, oracle_for, rows_of, run, subset
+from gpu_util import assert_fp8_parity, run, subset
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 B = pfkv.binding
-MODES = {"fp8p": (B.PRECISION_FP8_P, (0.25, FP8_MEAN_ERR_SIGMA)),
-         "fp8qp": (B.PRECISION_FP8, (0.35, 0.035))}
+MODES = {"fp8p": B.PRECISION_FP8_P, "fp8qp": B.PRECISION_FP8}
 mode_param = pytest.mark.parametrize("mode", sorted(MODES))
 
 
@@ -45,73 +46,70 @@ def _case(name, **over):
 @mode_param
 @pytest.mark.parametrize("name", ["tiny", "tiny_fixed_descale", "tiny_override_descale"])
 def test_fp8_tiny_parity(mode, name):
-    prec, bounds = MODES[mode]
-    if mode == "fp8qp" and name == "tiny_override_descale":
-        pytest.skip("reading A: near-one-hot softmax, e4m3 Q flips close maxima (measured 2.2 sigma)")
+    prec = MODES[mode]
     case = _case(name)
     out = run(case, num_segments=4, precision=prec)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), f"{mode} {name}", bounds)
+    assert_fp8_parity(out, case, prec, f"{mode} {name}")
 
 
 @mode_param
 @pytest.mark.parametrize("segments", [None, 1, 7, 64])
 def test_fp8_multigroup_parity(mode, segments):
-    prec, bounds = MODES[mode]
+    prec = MODES[mode]
     case = _case("multigroup")
     out = run(case, num_segments=segments, precision=prec)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), f"{mode} multigroup S={segments}", bounds)
+    assert_fp8_parity(out, case, prec, f"{mode} multigroup S={segments}")
 
 
 @mode_param
 def test_fp8_ragged_parity(mode):
-    prec, bounds = MODES[mode]
+    prec = MODES[mode]
     case = _case("ragged")
     out = run(case, precision=prec)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), f"{mode} ragged", bounds)
+    assert_fp8_parity(out, case, prec, f"{mode} ragged")
 
 
 @mode_param
 @pytest.mark.parametrize("group,q_lens", [(8, (4, 4, 4)), (8, (1, 3, 2)), (16, (3, 1, 2))])
 def test_fp8_group_and_qlen_parity(mode, group, q_lens):
-    prec, bounds = MODES[mode]
+    prec = MODES[mode]
     w = Workload(name="f8g", ctx=(8000, 3000, 700), q_lens=q_lens, num_q_heads=group, num_kv_heads=1,
                  num_segments=8, seed=41)
     case = make_case(w, "cpu").to(DEV)
     out = run(case, num_segments=8, precision=prec)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), f"{mode} G={group} q_lens={q_lens}", bounds)
+    assert_fp8_parity(out, case, prec, f"{mode} G={group} q_lens={q_lens}")
 
 
 @mode_param
 @pytest.mark.parametrize("segments", [1, 5])
 def test_fp8_long_segments_parity(mode, segments):
-    prec, bounds = MODES[mode]
+    prec = MODES[mode]
     w = Workload(name="longseg", ctx=(20000, 4100, 33), q_lens=(4, 1, 2), num_q_heads=16, num_kv_heads=1,
                  num_segments=segments, seed=36)
     case = make_case(w, "cpu").to(DEV)
     out = run(case, num_segments=segments, precision=prec)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), f"{mode} long segments S={segments}", bounds)
+    assert_fp8_parity(out, case, prec, f"{mode} long segments S={segments}")
 
 
 @mode_param
 @pytest.mark.parametrize("name", ["prod", "gqa8"])
 def test_fp8_full_size_all_rows(mode, name):
-    prec, bounds = MODES[mode]
+    prec = MODES[mode]
     w = workload(name)
     case = make_case(w, DEV)
     out = run(case, num_segments=w.num_segments, precision=prec)
     torch.cuda.synchronize()
-    ref = oracle_for(subset(case, list(range(w.num_seqs))))
-    assert_parity(out, ref, f"{mode} {name}, all {w.num_seqs} sequences", bounds)
+    assert_fp8_parity(out, subset(case, list(range(w.num_seqs))), prec, f"{mode} {name}, all {w.num_seqs} sequences")
 
 
 @mode_param
 def test_fp8_graph_replay_and_rerun_bitwise(mode):
-    FP8 = MODES[mode][0]
+    FP8 = MODES[mode]
     case = _case("tiny")
     S = 4
     out = torch.empty_like(case.q)
@@ -135,7 +133,7 @@ def test_fp8_graph_replay_and_rerun_bitwise(mode):
 
 @mode_param
 def test_fp8_page_permutation_bitwise(mode):
-    FP8 = MODES[mode][0]
+    FP8 = MODES[mode]
     case = _case("multigroup")
     a = run(case, num_segments=5, precision=FP8)
     b = run(permute_pool(case, seed=321), num_segments=5, precision=FP8)
@@ -146,10 +144,10 @@ def test_fp8_page_permutation_bitwise(mode):
 @mode_param
 @pytest.mark.parametrize("group,segments", [(16, 8), (8, 1)])
 def test_fp8_short_qlen_rows_match_verify_bitwise(mode, group, segments):
-    """Q is quantised per row, so a row's bits do not depend on the other rows of its call."""
+    """Q is quantised within its own row (per 32 dims), so a row's bits do not depend on the other rows of its call."""
     w = Workload(name="v", ctx=(5000, 777, 40, 16), q_lens=(4, 4, 4, 4), num_q_heads=group, num_kv_heads=1,
                  num_segments=segments, seed=34)
-    FP8 = MODES[mode][0]
+    FP8 = MODES[mode]
     case = make_case(w, "cpu").to(DEV)
     verify = run(case, num_segments=segments, precision=FP8)
     for q_len in (1, 2, 3):
@@ -164,14 +162,16 @@ def test_fp8_short_qlen_rows_match_verify_bitwise(mode, group, segments):
 
 
 @mode_param
-def test_fp8_dominant_key_flushes_small_probabilities(mode):
-    """The fp8-P underflow the aiter PR #7375 review works through: with one key
-    scoring 7 and 3999 keys scoring 0, P = e^-7 ~ 9e-4 of the maximum is below half
-    the smallest e4m3 subnormal (2^-10) and flushes to zero, so the output is V of
-    the dominant key (+1) instead of the exact (e^7 - 3999) / (e^7 + 3999) =
-    -0.5696 the 16-bit path returns."""
+@pytest.mark.parametrize("n,segments", [(4000, 1), (16384, 1), (16384, 8)])
+def test_fp8_dominant_key_keeps_small_probabilities(mode, n, segments):
+    """The fp8-P underflow the aiter PR #7375 review works through: one key scores
+    7 and n - 1 keys score 0, so every other P is e^-7 ~ 9e-4 of the maximum,
+    below half the smallest e4m3 subnormal (2^-10); unscaled e4m3 P flushes them
+    and returns V of the dominant key (+1). Under the power-of-two scale per 32
+    keys they keep 3 mantissa bits, and the output is the exact
+    (e^7 - (n - 1)) / (e^7 + (n - 1)) (-0.5696 at 4000 keys, -0.8745 at 16384)
+    to within the e4m3 rounding of e^-7 and the bf16 output."""
     from test_gpu_parity import _code, _one_sequence
-    n = 4000
     k = np.zeros((n, 1, 256), np.uint8)
     k[0, 0, 0] = _code(14.0)
     v = np.full((n, 1, 256), _code(-1.0), np.uint8)
@@ -180,14 +180,15 @@ def test_fp8_dominant_key_flushes_small_probabilities(mode):
     q[0, :, 0] = 8.0
     case = _one_sequence(k, v, q, 1)
     exact = (math.exp(7.0) - (n - 1)) / (math.exp(7.0) + (n - 1))
-    out16 = run(case, num_segments=1)
-    out8 = run(case, num_segments=1, precision=MODES[mode][0])
+    out16 = run(case, num_segments=segments)
+    out8 = run(case, num_segments=segments, precision=MODES[mode])
     torch.cuda.synchronize()
     got16 = out16.float().cpu().numpy()
     got8 = out8.float().cpu().numpy()
-    print(f"[dominant] 16-bit {got16[0, 0, 0]:.5f}  fp8 {got8[0, 0, 0]:.5f}  exact {exact:.5f}", flush=True)
+    print(f"[dominant] n={n} S={segments} 16-bit {got16[0, 0, 0]:.5f}  fp8 {got8[0, 0, 0]:.5f}  "
+          f"exact {exact:.5f}", flush=True)
     assert np.max(np.abs(got16 - exact)) < 1e-2
-    assert np.max(np.abs(got8 - 1.0)) < 1e-2
+    assert np.max(np.abs(got8 - exact)) < 1e-2
 
 
 @mode_param
@@ -197,7 +198,7 @@ def test_fp8_single_key_returns_v_exactly(mode):
     v = np.arange(256, dtype=np.uint8)[None, None, :] % 0x70
     q = np.ones((1, 16, 256), np.float32)
     case = _one_sequence(k, v, q, 1, vd=2.0)
-    out = run(case, num_segments=1, precision=MODES[mode][0])
-    ref = oracle_for(case)
+    out = run(case, num_segments=1, precision=MODES[mode])
+    ref = oracle.attend(**case.to("cpu").host_arrays())
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy(), ref.astype(np.float32))

@@ -11,6 +11,8 @@ exactly converted K, and the hardware exp2/log2 (about 1 ulp each), add about
 <= 2^-4) it is ln(1 + 2^-4) = 0.061, rounded up to 0.07.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -23,7 +25,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 B = pfkv.binding
 LSE_TOL = 1e-3
-LSE_TOL_FP8_P = 0.07
+# e4m3 P under its block scales is within 2^-4 of the exact P wherever it is
+# above 2^-13 of its block's largest (what lies below is negligible), so the
+# row sum, and exp(lse), is within a factor 1 + 2^-4
+LSE_TOL_FP8_P = math.log1p(2.0 ** -4) + 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)

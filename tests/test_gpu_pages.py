@@ -13,7 +13,7 @@ import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Workload, make_case
 
-from gpu_util import assert_parity, oracle_for, run
+from gpu_util import assert_fp8_parity, assert_parity, oracle_for, run
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -77,4 +77,4 @@ def test_page_64_lse_and_fp8_variant():
     assert np.abs(lse.cpu().numpy().astype(np.float64).T - ref).max() <= 1e-3
     out = run(case, num_segments=6, precision=pfkv.binding.PRECISION_FP8_P)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_for(case), "page 64 fp8 P", (0.25, 0.03))
+    assert_fp8_parity(out, case, 1, "page 64 fp8 P")

@@ -13,7 +13,7 @@ import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Workload, make_case
 
-from gpu_util import assert_parity, oracle_for
+from gpu_util import assert_fp8_parity, assert_parity, oracle_for
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -77,8 +77,7 @@ def test_qlen8_lse_window_and_sinks():
 
 def test_qlen8_fp8_variants():
     case = _case(8, seed=45)
-    ref = oracle_for(case)
-    for mode, bounds in ((1, (0.25, 0.03)), (2, (0.35, 0.035))):
+    for mode in (1, 2):
         out = _call(case, 4, precision=mode)
         torch.cuda.synchronize()
-        assert_parity(out, ref, f"q_len<=8 fp8 mode {mode}", bounds)
+        assert_fp8_parity(out, case, mode, f"q_len<=8 fp8 mode {mode}")

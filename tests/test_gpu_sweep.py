@@ -2,7 +2,8 @@
 group, KV heads, ragged query tokens (up to 8), context lengths, cache page
 size, segment count, left window, soft-cap, sinks, arithmetic, lse. Each case
 is checked against the oracle at the bar of its arithmetic (16-bit P: max 0.15
-sigma, mean 0.02 sigma, lse within 1e-3; fp8 variants: their bands). The cases
+sigma, mean 0.02 sigma, lse within 1e-3; fp8 variants: the fp8 bar of
+gpu_util.assert_fp8_parity). The cases
 are drawn once from a fixed seed, so a failure names a reproducible case. The
 fp8 variants are drawn with at least 256 visible keys per query (see below).
 """
@@ -15,11 +16,11 @@ import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Workload, make_case
 
-from gpu_util import assert_parity
+from gpu_util import assert_fp8_parity, assert_parity
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-BANDS = {0: (0.15, 0.02), 1: (0.25, 0.03), 2: (0.35, 0.035)}
+
 
 
 def _draw_cases(n=72, seed=2024):
@@ -39,10 +40,11 @@ def _draw_cases(n=72, seed=2024):
         sinks = bool(rng.integers(0, 2))
         precision = int(rng.choice([0, 0, 0, 1, 2]))
         if precision != 0:
-            # e4m3 Q and P are held to their bands only where every query sees
-            # a few hundred keys: with a handful of visible keys e4m3 Q flips
-            # close maxima (measured: 8 visible keys, 0.48 sigma for e4m3 Q/P,
-            # 0.14 for e4m3 P, 0.016 for the default arithmetic)
+            # e4m3 Q and P are drawn only where every query sees a few hundred
+            # keys: with a handful of visible keys e4m3 Q flips close maxima
+            # (measured: 8 visible keys, 0.48 sigma for e4m3 Q/P, 0.14 for e4m3 P,
+            # 0.016 for the default arithmetic), and which maxima flip depends on
+            # every rounding, so the fp64 model says little about a given case
             ctx = tuple(max(c, 256 + q) for c, q in zip(ctx, q_lens))
             window = -1 if window >= 0 and window < 256 else window
         cases.append(dict(id=k, group=group, hkv=hkv, max_q=max_q, q_lens=q_lens, ctx=ctx, page=page,
@@ -78,9 +80,10 @@ def test_sweep_case(c):
     arrs = case.to("cpu").host_arrays()
     opts = dict(window_left=c["window"], softcap=c["softcap"],
                 sinks=None if sinks is None else sinks.cpu().numpy())
-    ref = oracle.attend(**arrs, **opts)
-    assert_parity(out, ref, f"sweep case {c['id']}", BANDS[c["precision"]])
-    if c["precision"] == 0:
+    if c["precision"] != 0:
+        assert_fp8_parity(out, case, c["precision"], f"sweep case {c['id']}", **opts)
+    else:
+        assert_parity(out, oracle.attend(**arrs, **opts), f"sweep case {c['id']}")
         ref_lse = oracle.attend_lse(**arrs, **opts)
         got = lse.cpu().numpy().astype(np.float64).T
         assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))

@@ -14,7 +14,7 @@ import oracle
 import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd.workloads import Workload, make_case, workload
 
-from gpu_util import assert_parity, oracle_for, run
+from gpu_util import assert_fp8_parity, assert_parity, oracle_for, run
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -112,7 +112,7 @@ def test_token_pages_options_and_fp8():
     assert_parity(out, ref, "page 1 window/softcap/sinks")
     out8 = run(case, num_segments=6, precision=B.PRECISION_FP8_P)
     torch.cuda.synchronize()
-    assert_parity(out8, oracle_for(case), "page 1 fp8 P", (0.25, 0.03))
+    assert_fp8_parity(out8, case, 1, "page 1 fp8 P")
 
 
 def test_token_pages_eight_query_tokens():
