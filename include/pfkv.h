@@ -174,7 +174,10 @@ int pfkv_check_args(const pfkv_args* args, const char* arch, int num_cus);
  * the main kernel writes out itself and no reduce is enqueued (the workspace is
  * still validated but not touched). Validates with
  * pfkv_check_args against the current device first and checks that the device
- * pointers belong to it. Aliasing between out and any input is not allowed.
+ * pointers belong to it (each thread remembers the last 32 pointers it found to
+ * be device memory of a device and does not query them again, so a loop that
+ * passes the same buffers makes no queries). Aliasing between out and any
+ * input is not allowed.
  * Concurrent calls that share a workspace race; give each stream its own.
  */
 int pfkv_verify_attn_fwd(const pfkv_args* args, void* stream);

@@ -124,7 +124,27 @@ bool is_gfx950(const char* arch) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Pointers already found to be device memory of a device, per thread: the
+// last kCheckedSlots distinct (pointer, device) pairs. A serving loop that
+// passes the same buffers every call then makes no pointer queries (each costs
+// about a microsecond on the host). A buffer freed after a call and passed
+// again is not queried again; freed memory is the caller's error either way.
+constexpr int kCheckedSlots = 32;
+struct CheckedPointer {
+  const void* ptr;
+  int device;
+};
+thread_local CheckedPointer g_checked[kCheckedSlots];
+thread_local int g_checked_next = 0;
+
+bool already_checked(const void* ptr, int device) {
+  for (int i = 0; i < kCheckedSlots; ++i)
+    if (g_checked[i].ptr == ptr && g_checked[i].device == device && ptr != nullptr) return true;
+  return false;
+}
+
 int check_device_pointer(const void* ptr, int device, const char* name) {
+  if (already_checked(ptr, device)) return PFKV_OK;
   hipPointerAttribute_t attr;
   const hipError_t e = hipPointerGetAttributes(&attr, ptr);
   if (e != hipSuccess) {
@@ -136,6 +156,8 @@ int check_device_pointer(const void* ptr, int device, const char* name) {
   if (attr.device != device)
     return fail(PFKV_DEVICE, std::string(name) + " belongs to device " + std::to_string(attr.device) +
                                  ", not the current device " + std::to_string(device));
+  g_checked[g_checked_next] = CheckedPointer{ptr, device};
+  g_checked_next = (g_checked_next + 1) % kCheckedSlots;
   return PFKV_OK;
 }
 

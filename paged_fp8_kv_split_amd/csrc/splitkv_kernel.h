@@ -481,6 +481,17 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8&
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
 }
+// max of v over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one position in each of
+// the four 16-lane rows) by the row-swap permutes: each swap hands a lane its
+// partner row's value in one of its two results and keeps its own in the
+// other, with no LDS round trip
+__device__ __forceinline__ float rows_max(float v) {
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(v, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
+}
+
 __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
@@ -774,9 +785,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
     if (!F8P && __builtin_amdgcn_readfirstlane(flag_word) != 0) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        float v = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
+        const float v = rows_max(fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3])));
         if (g == 0) mx[(16 * rb + n) * kPagesPerStep + w] = v;
       }
       lds_barrier();   // the P.V waves take this barrier too
@@ -860,8 +869,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         over |= v > thr[rb];
         if constexpr (F8P) {
           // this page slot's row maximum, for the block scales of P (formed next phase)
-          float r = fmaxf(v, __shfl_xor(v, 16, 64));
-          r = fmaxf(r, __shfl_xor(r, 32, 64));
+          const float r = rows_max(v);
           if (g == 0) *(float*)(smem + C::kOffP + (kst & 1) * C::kPBytes + C::kP8Xmax + (16 * rb + n) * 16 + 4 * w) = r;
         }
       }

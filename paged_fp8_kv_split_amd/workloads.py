@@ -105,6 +105,8 @@ WORKLOADS = {
     # long context and occupancy pair
     "long": _uniform("long", 16, 70000, 4, 16, 1, 16, seed=4, replicas=16),
     "occupancy": _uniform("occupancy", 4, 35000, 4, 16, 1, 64, seed=44, replicas=16),
+    # decode: the production shape with one query token per sequence
+    "decode": _uniform("decode", 16, 35000, 1, 16, 1, 16, seed=7, replicas=16),
     # ragged draft-extend / decode and the multi-head-group pass
     "ragged": _ragged(5),
     "multigroup": _uniform("multigroup", 2, 777, 4, 32, 2, None, seed=5),

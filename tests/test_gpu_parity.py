@@ -337,6 +337,35 @@ def test_host_pointer_is_refused():
                          case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, num_segments=4)
 
 
+def test_host_pointer_is_refused_by_the_library_after_a_good_call():
+    """The C ABI's own pointer check (pfkv_verify_attn_fwd -> PFKV_DEVICE): a call
+    that passes host memory as block_tables is refused without a launch, also
+    right after a good call with the same other buffers (whose checks the
+    library remembers)."""
+    import ctypes
+    case = _case("tiny")
+    lib = pfkv.load_library()
+    out = torch.zeros_like(case.q)
+    ws = torch.empty(pfkv.workspace_bytes(4, case.q.shape[0], case.q.shape[1]), dtype=torch.uint8, device=DEV)
+    a = pfkv.binding.build_args(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                                case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, 4, out, ws)
+    handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.pfkv_verify_attn_fwd(ctypes.byref(a), handle) == 0
+    torch.cuda.synchronize()
+    good = out.clone()
+    host_table = case.block_tables.cpu().numpy().copy()
+    a.block_tables = host_table.ctypes.data
+    out.zero_()
+    assert lib.pfkv_verify_attn_fwd(ctypes.byref(a), handle) == 3
+    assert "block_tables" in pfkv.binding.last_error()
+    torch.cuda.synchronize()
+    assert not out.view(torch.int16).any()
+    a.block_tables = case.block_tables.data_ptr()
+    assert lib.pfkv_verify_attn_fwd(ctypes.byref(a), handle) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), good.view(torch.int16))
+
+
 @pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_stream_read_reads_every_byte(variant):
     """Each streaming-read variant folds every 32-bit word it reads into the sink
