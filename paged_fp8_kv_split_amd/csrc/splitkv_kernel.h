@@ -1365,16 +1365,22 @@ splitkv_main_kernel(MainParams p) {
     // Renumber them so that each XCD runs a contiguous run of ids (a whole
     // sequence's segments, when the grid allows): the sequence's queries and
     // block-table row are then fetched into one XCD's L2, not into all eight.
+    // The work-groups that read the same pages (the kv_split halves of a
+    // 32-head group and the q_split query blocks, z = hkv * nsplit + sub) are
+    // made neighbours in the new order, so that they run on one XCD at the
+    // same time and the second reader of each page finds it in that XCD's L2.
     // The renumbering is a bijection of [0, total) only while its 32-bit
     // arithmetic is exact: grids of 2^32 work-groups or more keep their ids.
     const uint64_t total64 = (uint64_t)gridDim.x * gridDim.y * gridDim.z;
     if ((total64 & 7u) == 0 && total64 <= 0xffffffffull) {
       const unsigned gx = gridDim.x, gxy = gx * gridDim.y, total = (unsigned)total64;
+      const unsigned nsplit = (unsigned)(p.kv_split * p.q_split);
       const unsigned id = blockIdx.x + gx * (blockIdx.y + gridDim.y * blockIdx.z);
       const unsigned r = (id & 7u) * (total >> 3) + (id >> 3);
-      geo.seg = (int)(r % gx);
-      geo.b = (int)((r / gx) % gridDim.y);
-      wg_z = (int)(r / gxy);
+      const unsigned rr = r / nsplit;
+      geo.seg = (int)(rr % gx);
+      geo.b = (int)((rr / gx) % gridDim.y);
+      wg_z = (int)((rr / gxy) * nsplit + r % nsplit);
     }
   }
   // BAL: balanced segments (a separate instantiation, so that the default
