@@ -226,7 +226,11 @@ int pfkv_segment_reduce(const pfkv_args* args, void* stream);
  * Segment-count heuristic (aiter PR #5190, Modifications: a helper that picks
  * the number of segments; Kernel notes: one work-group per CU):
  * clamp(num_cus / (num_seqs * num_kv_heads), 1, 64). Pure; returns 0 for
- * non-positive inputs.
+ * non-positive inputs. A call runs num_seqs * num_kv_heads * kv_split * q_split
+ * work-groups per segment (pfkv_verify_attn_fwd); passing num_kv_heads *
+ * kv_split * q_split as num_kv_heads keeps one work-group per CU for 32 query
+ * heads per KV head or more than 4 query tokens with 16 query heads per
+ * work-group.
  */
 int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
 
