@@ -97,7 +97,7 @@ def test_fp8_long_segments_parity(mode, segments):
 
 
 @mode_param
-@pytest.mark.parametrize("name", ["prod", "gqa8"])
+@pytest.mark.parametrize("name", ["prod", "gqa8", "decode"])
 def test_fp8_full_size_all_rows(mode, name):
     prec = MODES[mode]
     w = workload(name)

@@ -97,7 +97,7 @@ def test_long_segments_parity(segments):
 
 
 # ------------------------------------------------------------------ full-size shapes, every row
-@pytest.mark.parametrize("name", ["prod", "gqa8", "long", "occupancy"])
+@pytest.mark.parametrize("name", ["prod", "gqa8", "long", "occupancy", "decode"])
 def test_full_size_all_rows(name):
     """The full-size shapes in the bench's launch configuration, every output
     row of every sequence against the oracle (which reads only the pages the
