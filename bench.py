@@ -23,6 +23,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -74,11 +75,17 @@ def warm_up(fn, min_calls, torch, seconds=WARMUP_SECONDS):
 
 
 def kernel_source_digest():
-    """Digest of the main kernel's sources (the templates and the 16-bit instantiation)."""
+    """Digest of the main kernel's sources (the templates and the 16-bit
+    instantiation) with comments and blank lines removed, so that a change to
+    the code changes it and a change to a comment does not."""
     h = hashlib.sha256()
     for name in ("splitkv_kernel.h", "splitkv_main.hip", "pfkv_internal.h"):
-        with open(os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -53,6 +53,17 @@
 // * Epilogue (16-bit arithmetic): o = O / l leaves the P.V waves' registers
 //   through a transpose inside groups of lanes (DPP swaps) and goes straight
 //   to memory, each row as runs of contiguous 8-byte stores.
+// * The opt-in fp8 modes (splitkv_main_fp8p.hip, splitkv_main_fp8.hip) round P
+//   to e4m3 under a power-of-two scale per (row, 32-key block), which the
+//   scaled fp8 MFMA takes in its A-scale operand, and follow each row's
+//   running maximum exactly (no slack), so that a row's largest weight is
+//   exact in e4m3. With e4m3 Q as well, Q is quantised per 32 dims and its
+//   scales ride in the score MFMA's B-scale operand.
+// * Work-group ids are renumbered so that each XCD runs a contiguous run of
+//   them (a whole sequence's segments where the grid allows), with the
+//   work-groups that read the same pages (the two halves of 32 query heads per
+//   KV head, the two query blocks of an 8-token draft) next to each other, so
+//   that the second read of a page comes from that XCD's L2.
 #pragma once
 
 #include <type_traits>
