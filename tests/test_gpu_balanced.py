@@ -13,7 +13,7 @@ import paged_fp8_kv_split_amd as pfkv
 from paged_fp8_kv_split_amd import binding
 from paged_fp8_kv_split_amd.workloads import Workload, make_case, workload
 
-from gpu_util import assert_parity, oracle_for
+from gpu_util import assert_fp8_parity, assert_parity, oracle_for
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -154,3 +154,13 @@ def test_stale_workspace_does_not_leak(balanced):
     (o0, l0), (o1, l1) = outs
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
     assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_balanced_fp8_variants(mode):
+    """The fp8 arithmetic under the balanced schedule (up to 128 segments, the
+    eight-wave reduce), at the fp8 bar of gpu_util.assert_fp8_parity."""
+    case = make_case(workload("ragged"), "cpu").to(DEV)
+    out = _run(case, 128, precision=mode)
+    torch.cuda.synchronize()
+    assert_fp8_parity(out, case, mode, f"balanced ragged precision={mode}")
