@@ -65,6 +65,29 @@ def test_ragged_balanced():
     _both(case, 40)
 
 
+def test_graph_capture_replays_bitwise():
+    """The use the entry point exists for: a call captured into a HIP graph (no
+    allocation inside the capture), replayed with eager work in between."""
+    case = make_case(workload("tiny"), "cpu").to(DEV)
+    ref = pfkv.verify_attn(*_args(case), num_segments=4)
+    out = torch.zeros_like(case.q)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        binding.verify_attn_noalloc(*_args(case), 4, out, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        binding.verify_attn_noalloc(*_args(case), 4, out, stream=stream)
+    for k in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), k
+        other = pfkv.verify_attn(*_args(case), num_segments=4)
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), ref.view(torch.int16))
+
+
 def test_beyond_limit_is_rejected():
     case = make_case(Workload(name="tiny", ctx=(64,), q_lens=(4,), num_q_heads=16, num_kv_heads=1,
                               num_segments=None, seed=9), "cpu").to(DEV)
