@@ -745,12 +745,12 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   // is not rounded. The page slots' row maxima of step u are already in LDS
   // (exchanged in the phase that computed the scores for the block scales), so
   // the flagged update reads them there, without the slow path's extra
-  // barrier. Page slots w and w ^ 2 form
-  // the 32-key block (w & 1) of P in the P.V MFMA: the block's largest P,
-  // 2^(top c2 - m) <= 1, sets a power of two 2^e that puts it in [128, 256)
-  // before rounding to e4m3 (e <= -7); a block below 2^-100 contributes
-  // nothing (shift +inf: every P of it is 0, e = 0), so e >= -107. 2^-e is
-  // folded into the exponent; the scale rides in the MFMA's A-scale operand.
+  // barrier. Page slots w and w ^ 2 form the 32-key block (w & 1) of P in the
+  // P.V MFMA: the block's largest P, 2^(top c2 - m) <= 1, sets a power of two
+  // 2^e that puts it in [128, 256) before rounding to e4m3 (e <= -7); a block
+  // below 2^-100 contributes nothing (shift +inf: every P of it is 0, e = 0),
+  // so e >= -107. 2^-e is folded into the exponent; the scale rides in the
+  // MFMA's A-scale operand.
   auto form_p = [&](int u, int pbuf, unsigned flag_word) {
     f32x4 pv[NRB];
     float top[F8P ? NRB : 1], shift[F8P ? NRB : 1];
