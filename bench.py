@@ -325,10 +325,10 @@ def main():
     T, Hq = w.total_q, w.num_q_heads
     out = torch.empty((T, Hq, w.head_dim), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device="cuda")
-    def make_refs(prec):
+    def make_refs(prec, merge_sync=None):
         argv = [binding.build_args(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.cu_seqlens_q,
                                    c.k_descale, c.v_descale, c.softmax_scale, S, out, ws, prec,
-                                   balance_segments=args.balance) for c in cases]
+                                   balance_segments=args.balance, merge_sync=merge_sync) for c in cases]
         return argv, [ctypes.byref(a) for a in argv]
 
     argv, refs = make_refs(PRECISIONS[args.precision][0])
@@ -446,6 +446,28 @@ def main():
         variants[other_name] = {"us_per_call": round(other_us, 2),
                                 "value": round(w.kv_bytes / (other_us * 1e-6) / 1e12, 4)}
         log(f"{other_name} variant: {other_us:.2f} us/call, {variants[other_name]['value']:.3f} TB/s")
+
+    # ---- the in-launch merge (merge_sync): the same calls with the merge in
+    # the main launch where the call allows it (else the two launches run)
+    sync = pfkv.merge_sync_buffer(w.num_seqs, Hq, "cuda")
+    argv_m, refs_m = make_refs(PRECISIONS[args.precision][0], sync)
+    warm_up(lambda k: lib.pfkv_verify_attn_fwd(refs_m[k % R], handle), args.warmup, torch, args.warmup_seconds)
+    torch.cuda.synchronize()
+    merge_served = bool((sync.view(torch.int32)[0].item() >> 8) != 0)
+    v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v0.record(stream)
+    for k in range(args.steps):
+        st = lib.pfkv_verify_attn_fwd(refs_m[k % R], handle)
+        if st != 0:
+            raise binding.PfkvError(st, binding.last_error())
+    v1.record(stream)
+    torch.cuda.synchronize()
+    merge_us = v0.elapsed_time(v1) * 1e3 / args.steps
+    variants["in_launch_merge"] = {"us_per_call": round(merge_us, 2),
+                                   "value": round(w.kv_bytes / (merge_us * 1e-6) / 1e12, 4),
+                                   "served": merge_served}
+    log(f"in-launch merge variant ({'served' if merge_served else 'not served: two launches'}): "
+        f"{merge_us:.2f} us/call, {variants['in_launch_merge']['value']:.3f} TB/s")
 
     if args.copy_calibration:
         # an elementwise kernel (not a DMA-engine memcpy), so counters see it as a dispatch

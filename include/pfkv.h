@@ -87,7 +87,35 @@ typedef struct pfkv_args {
   int32_t balance_segments;    /* 0 (default): every sequence is cut into num_segments segments. 1: segments
                                   in proportion to each sequence's pages (see below); num_segments (2..128)
                                   is then the cap per sequence and num_seqs must be <= 1024 */
+  void* merge_sync;            /* optional, NULL (default) = off: sync words of the in-launch merge (below),
+                                  256-B aligned, zero before the first call that uses them */
+  uint64_t merge_sync_size;    /* bytes at merge_sync */
+  int32_t merge_wait_us;       /* in-launch merge: how long a work-group waits for the rest of its group;
+                                  0 (default) = 50 us; < 0 = not at all (each work-group that is not the last
+                                  of its group hands its rows to the last: slower, same bits) */
 } pfkv_args;
+
+/*
+ * In-launch merge (opt-in). The segment reduce is a second launch, which costs
+ * about 5 us after a 55 us main kernel and more, relative to the call, on
+ * short contexts with many segments; aiter PR #5190 (Microbenchmark, the S = 64
+ * row of the bandwidth sweep) and SGLang PR #37465 (Draft shapes, decode) time
+ * such calls. With merge_sync set, pfkv_verify_attn_fwd (and the
+ * allocation-free entry point) run the merge inside the main launch when the
+ * call allows it: 16-bit arithmetic, head_dim 256, page_size >= 16, no balanced
+ * segments, num_segments >= 2, and a grid of at most one work-group per CU.
+ * Other calls run the two launches and leave merge_sync untouched. The result
+ * is bit for bit that of the two launches.
+ * The work-groups of a (sequence, head group) count their arrivals in
+ * merge_sync; once all have written their partials each merges a share of the
+ * group's rows with the reduce's arithmetic. A work-group waits at most
+ * merge_wait_us for the others (so none waits on one that cannot start) and
+ * otherwise hands its share to the last arrival. The words must be zero
+ * before the first call that uses them; every call leaves them ready for the
+ * next. Calls that use the same words concurrently race: give each stream its
+ * own. Size: at least pfkv_merge_sync_bytes(num_seqs, num_q_heads) bytes.
+ */
+uint64_t pfkv_merge_sync_bytes(int num_seqs, int num_q_heads);
 
 /*
  * Balanced segments (balance_segments = 1), for batches whose contexts differ

@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     PfkvError,
     library_path,
     load_library,
+    merge_sync_buffer,
+    merge_sync_bytes,
     num_segments,
     prefill_attn,
     set_debug,

@@ -106,6 +106,9 @@ class PfkvArgs(ctypes.Structure):
         ("softcap", ctypes.c_float),
         ("max_q_len", ctypes.c_int32),
         ("balance_segments", ctypes.c_int32),
+        ("merge_sync", ctypes.c_void_p),
+        ("merge_sync_size", ctypes.c_uint64),
+        ("merge_wait_us", ctypes.c_int32),
     ]
 
 
@@ -136,6 +139,8 @@ def load_library():
     lib.pfkv_num_segments.restype = ctypes.c_int
     lib.pfkv_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.pfkv_workspace_bytes.restype = ctypes.c_uint64
+    lib.pfkv_merge_sync_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.pfkv_merge_sync_bytes.restype = ctypes.c_uint64
     lib.pfkv_last_error.argtypes = []
     lib.pfkv_last_error.restype = ctypes.c_char_p
     lib.pfkv_device_info.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -189,6 +194,18 @@ def workspace_bytes(num_segments_: int, total_q: int, num_q_heads: int) -> int:
     return int(load_library().pfkv_workspace_bytes(int(num_segments_), int(total_q), int(num_q_heads)))
 
 
+def merge_sync_bytes(num_seqs: int, num_q_heads: int) -> int:
+    return int(load_library().pfkv_merge_sync_bytes(int(num_seqs), int(num_q_heads)))
+
+
+def merge_sync_buffer(num_seqs: int, num_q_heads: int, device) -> torch.Tensor:
+    """Zeroed sync words for the in-launch merge (``merge_sync=`` of
+    :func:`verify_attn`), for calls of up to ``num_seqs`` sequences and
+    ``num_q_heads`` query heads. Keep it and pass it to every call on one
+    stream: each call leaves it ready for the next."""
+    return torch.zeros(max(merge_sync_bytes(num_seqs, num_q_heads), 256), dtype=torch.uint8, device=device)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -208,12 +225,15 @@ PRECISION_FP8 = 2     # e4m3 Q (per-row scale) and e4m3 P on the fp8 MFMA
 
 def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                softmax_scale, num_segments_, out, workspace, precision=PRECISION_16BIT, lse=None,
-               sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=0) -> PfkvArgs:
+               sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=0, merge_sync=None,
+               merge_wait_us=0) -> PfkvArgs:
     """Fill a ``pfkv_args`` from torch tensors (shapes and dtypes checked here).
 
     ``lse`` (optional) is a contiguous float32 ``[Hq, T]`` tensor on q's device,
     ``sinks`` (optional) a contiguous float32 ``[Hq]`` tensor on q's device.
     ``workspace`` may be None (pointer NULL, size 0) for the allocation-free call.
+    ``merge_sync`` (optional) is a contiguous uint8 tensor on q's device
+    (:func:`merge_sync_buffer`).
     """
     k_cache, v_cache = _as_bytes(k_cache), _as_bytes(v_cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
@@ -285,13 +305,21 @@ def build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_desc
     a.softcap = float(softcap)
     a.max_q_len = int(max_q_len)
     a.balance_segments = 1 if balance_segments else 0
+    if merge_sync is not None:
+        if merge_sync.dtype != torch.uint8 or not merge_sync.is_contiguous():
+            raise TypeError("merge_sync must be a contiguous uint8 tensor")
+        if merge_sync.device != q.device:
+            raise ValueError(f"merge_sync must be on q's device ({q.device}), got {merge_sync.device}")
+        a.merge_sync = merge_sync.data_ptr()
+        a.merge_sync_size = merge_sync.numel()
+    a.merge_wait_us = int(merge_wait_us)
     return a
 
 
 def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                 softmax_scale, num_segments=None, out=None, workspace=None, stream=None,
                 precision=PRECISION_16BIT, return_lse=False, lse=None, sinks=None, window_left=-1,
-                softcap=0.0, max_q_len=0, balance_segments=False):
+                softcap=0.0, max_q_len=0, balance_segments=False, merge_sync=None, merge_wait_us=0):
     """Split-KV verify attention; returns ``out`` (bf16 ``[T, Hq, 256]``), or
     ``(out, lse)`` when ``return_lse`` is set or an ``lse`` buffer is given.
 
@@ -307,8 +335,11 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
     ``precision`` selects the main kernel's arithmetic (``PRECISION_16BIT``,
     ``PRECISION_FP8_P`` or ``PRECISION_FP8``, see ``include/pfkv.h``).
     ``workspace`` (uint8, at least :func:`workspace_bytes` bytes) is allocated with
-    torch when not given. The call is enqueued on ``stream`` (default: torch's
-    current stream) and does not synchronize.
+    torch when not given. ``merge_sync`` (:func:`merge_sync_buffer`, kept across
+    calls) runs the merge inside the main launch where the call allows it
+    (``include/pfkv.h``); ``merge_wait_us`` bounds its waits. The call is
+    enqueued on ``stream`` (default: torch's current stream) and does not
+    synchronize.
     """
     lib = load_library()
     if not q.is_cuda:
@@ -328,7 +359,7 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                    softmax_scale, num_segments, out, workspace, precision, lse, sinks, window_left, softcap,
-                   max_q_len, balance_segments)
+                   max_q_len, balance_segments, merge_sync, merge_wait_us)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -338,7 +369,8 @@ def verify_attn(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_des
 
 def verify_attn_noalloc(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                         softmax_scale, num_segments, out, stream=None, precision=PRECISION_16BIT, lse=None,
-                        sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=False):
+                        sinks=None, window_left=-1, softcap=0.0, max_q_len=0, balance_segments=False,
+                        merge_sync=None, merge_wait_us=0):
     """The allocation-free call (``pfkv_verify_attn_fwd_noalloc``): the caller
     passes ``out`` (and ``lse`` if wanted) and an explicit ``num_segments``;
     the partials go to the library's own device array, so neither this wrapper
@@ -348,7 +380,7 @@ def verify_attn_noalloc(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_
         raise ValueError("q must be a GPU tensor")
     a = build_args(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, k_descale, v_descale,
                    softmax_scale, num_segments, out, None, precision, lse, sinks, window_left, softcap,
-                   max_q_len, balance_segments)
+                   max_q_len, balance_segments, merge_sync, merge_wait_us)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

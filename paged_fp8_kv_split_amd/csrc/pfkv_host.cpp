@@ -161,6 +161,24 @@ int check_device_pointer(const void* ptr, int device, const char* name) {
   return PFKV_OK;
 }
 
+// Split of a sequence's query heads and tokens over work-groups (blockIdx.z):
+// kv_split = 2 when 32 query heads share a KV head; q_split = 2 when 16 query
+// heads per work-group meet more than 4 query tokens (a work-group stacks at
+// most kMaxRows = 64 query rows).
+int kv_split_of(const pfkv_args* a) { return a->num_q_heads / a->num_kv_heads == 32 ? 2 : 1; }
+int q_per_wg_of(const pfkv_args* a) {
+  const int group = a->num_q_heads / a->num_kv_heads;
+  return std::min(pfkv::kMaxRows / (group == 32 ? 16 : group), pfkv::kMaxQLen);
+}
+int q_split_of(const pfkv_args* a) {
+  const int max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
+  return (max_q_len + q_per_wg_of(a) - 1) / q_per_wg_of(a);
+}
+// merge groups (blockIdx.z values) per sequence
+uint64_t merge_groups_per_seq(const pfkv_args* a) {
+  return (uint64_t)a->num_kv_heads * kv_split_of(a) * q_split_of(a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +197,13 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads) {
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads) {
   if (num_segments <= 0 || total_q <= 0 || num_q_heads <= 0) return 0;
   return (uint64_t)num_segments * (uint64_t)total_q * (uint64_t)num_q_heads * pfkv::kPartialBytes;
+}
+
+uint64_t pfkv_merge_sync_bytes(int num_seqs, int num_q_heads) {
+  // merge groups per sequence: num_kv_heads * kv_split * q_split <= num_q_heads / 4
+  if (num_seqs <= 0 || num_q_heads <= 0) return 0;
+  const uint64_t groups = (uint64_t)num_seqs * (uint64_t)((num_q_heads + 3) / 4);
+  return groups * pfkv::kMergeSyncWords * 4;
 }
 
 int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
@@ -245,6 +270,14 @@ int pfkv_check_args(const pfkv_args* a, const char* arch, int num_cus) {
   if (a->workspace_size < need)
     return fail(PFKV_INVALID, "workspace too small: need " + std::to_string(need) + " bytes, got " +
                                   std::to_string(a->workspace_size));
+  if (a->merge_sync != nullptr) {
+    if (!aligned(a->merge_sync, 256)) return fail(PFKV_INVALID, "merge_sync must be 256-byte aligned");
+    const uint64_t need_sync = (uint64_t)a->num_seqs * merge_groups_per_seq(a) * pfkv::kMergeSyncWords * 4;
+    if (a->merge_sync_size < need_sync)
+      return fail(PFKV_INVALID, "merge_sync too small: need " + std::to_string(need_sync) + " bytes, got " +
+                                    std::to_string(a->merge_sync_size));
+  }
+  if (a->merge_wait_us > 100000) return fail(PFKV_INVALID, "merge_wait_us must be <= 100000");
 
   // Supported envelope of the kernels.
   if (!is_gfx950(arch)) return fail(PFKV_UNSUPPORTED, std::string("device is ") + arch + ", kernels are gfx950");
@@ -343,15 +376,9 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bo
   m.window_left = a->window_keys > 0 ? a->window_keys - 1 : -1;
   m.softcap = a->softcap;
   m.direct = a->num_segments == 1 ? 1 : 0;
-  m.kv_split = group == 32 ? 2 : 1;
-  {
-    // a work-group stacks at most kMaxRows = 64 query rows: with 16 query heads
-    // per work-group and up to 8 tokens, a sequence's tokens split in two blocks
-    const int g_wg = group == 32 ? 16 : group;
-    const int max_q_len = a->max_q_len > 0 ? a->max_q_len : pfkv::kDefaultMaxQLen;
-    m.q_per_wg = std::min(pfkv::kMaxRows / g_wg, pfkv::kMaxQLen);
-    m.q_split = (max_q_len + m.q_per_wg - 1) / m.q_per_wg;
-  }
+  m.kv_split = kv_split_of(a);
+  m.q_per_wg = q_per_wg_of(a);
+  m.q_split = q_split_of(a);
   m.precision = a->precision;
   m.head_dim = a->head_dim;
   m.num_seqs = a->num_seqs;
@@ -371,6 +398,21 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bo
     m.num_slots = std::max(a->num_seqs, std::max(1, d.num_cus / per_slot));
   }
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
+  m.merge_sync = nullptr;
+  if (a->merge_sync != nullptr) {
+    st = check_device_pointer(a->merge_sync, device, "merge_sync");
+    if (st != PFKV_OK) return st;
+    // every work-group of the grid resident at once (one per CU), so that the
+    // waits of a group normally end by its last arrival, not by the time limit
+    // (and o partials under 2^31 bytes, the reach of the merge's buffer loads)
+    const uint64_t wgs = (uint64_t)a->num_segments * a->num_seqs * merge_groups_per_seq(a);
+    if (a->precision == PFKV_PRECISION_16BIT && a->head_dim == 256 && a->page_size >= 16 && !m.balance &&
+        a->num_segments >= 2 && wgs <= (uint64_t)d.num_cus && part_rows * pfkv::kHeadDim * 2 < (1ull << 31)) {
+      m.merge_sync = (uint32_t*)a->merge_sync;
+      m.merge_wait_ticks = a->merge_wait_us == 0 ? pfkv::kMergeWaitTicksDefault
+                                                 : (a->merge_wait_us < 0 ? 0u : (uint32_t)a->merge_wait_us * 100u);
+    }
+  }
 
   rp->ws_o = ws_o;
   rp->ws_ml = ws_ml;
@@ -430,7 +472,7 @@ int verify_attn_library_workspace(const pfkv_args* a, void* ws, uint64_t ws_byte
   pfkv::ReduceParams rp;
   int st = prepare(&b, &mp, &rp, /*library_workspace=*/true);
   if (st == PFKV_OK) st = launch_main(mp, b.num_q_heads / b.num_kv_heads, stream);
-  if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);
+  if (st == PFKV_OK && !mp.direct && mp.merge_sync == nullptr) st = launch_reduce(rp, stream);
   return st;
 }
 
@@ -453,7 +495,8 @@ int pfkv_verify_attn_fwd(const pfkv_args* a, void* stream) {
   int st = prepare(a, &mp, &rp);
   if (st == PFKV_OK && debug_enabled()) st = debug_check(a, stream);
   if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
-  if (st == PFKV_OK && !mp.direct) st = launch_reduce(rp, stream);   // one segment: out is final
+  // one segment, or the merge inside the main launch: out is final
+  if (st == PFKV_OK && !mp.direct && mp.merge_sync == nullptr) st = launch_reduce(rp, stream);
   return st;
 }
 
@@ -461,6 +504,7 @@ int pfkv_splitkv_main(const pfkv_args* a, void* stream) {
   pfkv::MainParams mp;
   pfkv::ReduceParams rp;
   int st = prepare(a, &mp, &rp);
+  mp.merge_sync = nullptr;   // this stage writes the partials only
   if (st == PFKV_OK && debug_enabled()) st = debug_check(a, stream);
   if (st == PFKV_OK) st = launch_main(mp, a->num_q_heads / a->num_kv_heads, stream);
   return st;

@@ -24,6 +24,14 @@ constexpr int kMaxBalancedSegments = 128;   // the cap per sequence with balance
 // so that segment s contributes  2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
 constexpr int kPartialBytes = kHeadDim * 2 + 2 * 4;   // workspace bytes per (segment, token, head)
 
+// In-launch merge (opt-in): 32-bit sync words per merge group, a (sequence,
+// blockIdx.z) pair of the main grid: [0] arrivals (bits 0-7) and generation
+// (bits 8-31), [64..65] the 64-bit mask of shares handed to the last arrival,
+// on separate 128-byte lines. Zero before the first call; every call leaves
+// arrivals and mask at zero and the generation one higher.
+constexpr int kMergeSyncWords = 128;
+constexpr unsigned kMergeWaitTicksDefault = 5000;   // 50 us of the 100 MHz constant clock
+
 struct MainParams {
   const uint16_t* q;           // bf16 bits
   int64_t q_stride_token, q_stride_head;
@@ -65,6 +73,12 @@ struct MainParams {
   // sequence gets segment_count() of them (num_segments is the cap), the slots
   // in sequence order; blockIdx.y is 0 and slots past the last one stay idle
   int32_t balance, num_slots;
+  // in-launch merge (launched only with the merge instantiation, else NULL):
+  // kMergeSyncWords words per merge group, group (b, z) at
+  // merge_sync[(b * gridDim.z + z) * kMergeSyncWords]; a work-group waits at
+  // most merge_wait_ticks ticks of the 100 MHz clock for the rest of its group
+  uint32_t* merge_sync;
+  uint32_t merge_wait_ticks;
 };
 
 struct ReduceParams {

@@ -69,6 +69,7 @@
 #include <type_traits>
 
 #include "pfkv_internal.h"
+#include "segment_merge.h"
 
 namespace pfkv {
 namespace {
@@ -247,6 +248,20 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(unsigned lo, unsigned hi) {
 }
 
 // Geometry of one work-group's (segment, sequence, KV head), uniform.
+// A store of the segment partials: streaming (read once, by the reduce), or
+// with WT (the in-launch merge) a device-scope store, which completes only
+// once the value has reached the device's coherence point, so that a
+// work-group on another XCD reads it there without any cache maintenance.
+template <bool WT, typename T>
+__device__ __forceinline__ void partial_store(T v, T* dst) {
+  if constexpr (!WT)
+    __builtin_nontemporal_store(v, dst);
+  else if constexpr (sizeof(T) == 8)
+    __hip_atomic_store((uint64_t*)dst, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct Geo {
   int seg, b, h;     // h: this work-group's group of G query heads (query heads h G .. h G + G - 1)
   int hkv;           // the KV head those query heads read
@@ -512,7 +527,7 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // Q is quantised to e4m3 with a power-of-two scale per 32 dims and S^T runs on
 // the scaled fp8 MFMA; with F8P, P is rounded to e4m3 with a power-of-two
 // scale per (row, 32 keys).
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool WT = false>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G, D>;
   using Dm = Dim<D>;
@@ -960,8 +975,10 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
         } else {
           float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
           // streaming stores: the partials are read once, by the reduce
-          __builtin_nontemporal_store(m_ref[rb], dst);
-          __builtin_nontemporal_store(l, dst + 1);
+          // (WT: written through to the device's coherence point for the
+          // in-launch merge)
+          partial_store<WT>(m_ref[rb], dst);
+          partial_store<WT>(l, dst + 1);
         }
       }
     }
@@ -976,7 +993,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 // NRB row blocks; stages its slice of the segment's normalised output o. With
 // F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
 // e4m3 bytes.
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool WT = false>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G, D>;
   using Dm = Dim<D>;
@@ -1336,9 +1353,9 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
             } else {
               uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + dim0;
               if constexpr (NDB == 4)
-                __builtin_nontemporal_store(u32x2{wd[0], wd[1]}, (u32x2*)dst);
+                partial_store<WT>(u32x2{wd[0], wd[1]}, (u32x2*)dst);
               else
-                __builtin_nontemporal_store(wd[0], (unsigned*)dst);
+                partial_store<WT>(wd[0], (unsigned*)dst);
             }
           }
         }
@@ -1350,16 +1367,17 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   }
 }
 
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool WT = false>
 __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
   if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
+    score_wave<G, NRB, MODE, TOK, D, WT>(p, geo, smem);
   else
-    pv_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
+    pv_wave<G, NRB, MODE, TOK, D, WT>(p, geo, smem);
 }
 
-// TOK: the cache has one-token pages; D: head dim
-template <int G, int MODE, bool TOK, int D, bool BAL>
+// TOK: the cache has one-token pages; D: head dim; MERGE: the in-launch merge
+// (merge::merge_in_launch) follows the segment
+template <int G, int MODE, bool TOK, int D, bool BAL, bool MERGE = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
   using C = Cfg<G, D>;
@@ -1447,25 +1465,51 @@ splitkv_main_kernel(MainParams p) {
   geo.c2 = *(const const_f32*)p.k_descale * p.score_scale_log2;
 
   const int nrb = (geo.rows + 15) >> 4;
+  const int merge_group = geo.b * (int)gridDim.z + wg_z;
   if constexpr (G == 16) {
     switch (nrb) {
-      case 1: verify_segment<16, 1, MODE, TOK, D>(p, geo, smem); break;
-      case 2: verify_segment<16, 2, MODE, TOK, D>(p, geo, smem); break;
-      case 3: verify_segment<16, 3, MODE, TOK, D>(p, geo, smem); break;
-      default: verify_segment<16, 4, MODE, TOK, D>(p, geo, smem); break;
+      case 1: verify_segment<16, 1, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      case 2: verify_segment<16, 2, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      case 3: verify_segment<16, 3, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      default: verify_segment<16, 4, MODE, TOK, D, MERGE>(p, geo, smem); break;
     }
   } else if constexpr (G == 8) {
     switch (nrb) {
-      case 1: verify_segment<8, 1, MODE, TOK, D>(p, geo, smem); break;
-      case 2: verify_segment<8, 2, MODE, TOK, D>(p, geo, smem); break;
-      case 3: verify_segment<8, 3, MODE, TOK, D>(p, geo, smem); break;
-      default: verify_segment<8, 4, MODE, TOK, D>(p, geo, smem); break;
+      case 1: verify_segment<8, 1, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      case 2: verify_segment<8, 2, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      case 3: verify_segment<8, 3, MODE, TOK, D, MERGE>(p, geo, smem); break;
+      default: verify_segment<8, 4, MODE, TOK, D, MERGE>(p, geo, smem); break;
     }
   } else {
     if (nrb == 1)
-      verify_segment<4, 1, MODE, TOK, D>(p, geo, smem);
+      verify_segment<4, 1, MODE, TOK, D, MERGE>(p, geo, smem);
     else
-      verify_segment<4, 2, MODE, TOK, D>(p, geo, smem);
+      verify_segment<4, 2, MODE, TOK, D, MERGE>(p, geo, smem);
+  }
+  if constexpr (MERGE) {
+    // the segment reduce's per-row arithmetic, on this group's rows
+    ReduceParams rp = {};
+    rp.ws_o = p.ws_o;
+    rp.ws_ml = p.ws_ml;
+    rp.v_descale = p.v_descale;
+    rp.out = p.out;
+    rp.out_stride_token = p.out_stride_token;
+    rp.out_stride_head = p.out_stride_head;
+    rp.lse = p.lse;
+    rp.sinks = p.sinks;
+    rp.total_q = p.total_q;
+    rp.num_q_heads = p.num_q_heads;
+    rp.num_segments = p.num_segments;
+    rp.head_dim = p.head_dim;
+    uint32_t* sync = p.merge_sync + (int64_t)merge_group * kMergeSyncWords;
+    const int S = p.num_segments;
+    // the summation order of the segment reduce for S (waves per row there; S <= 64 here)
+    if (S <= 16)
+      merge::merge_in_launch<1, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
+    else if (S <= 32)
+      merge::merge_in_launch<2, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
+    else
+      merge::merge_in_launch<4, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
   }
 }
 
@@ -1484,6 +1528,20 @@ hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
       hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
     else
       return hipErrorInvalidValue;
+  } else if (p.merge_sync != nullptr) {
+    // the in-launch merge: 16-bit arithmetic, head dim 256, pages of 16 or more
+    if constexpr (MODE == kMode16 && !TOK && D == 256) {
+      if (group == 16)
+        hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+      else if (group == 8)
+        hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+      else if (group == 4)
+        hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+      else
+        return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     if (group == 16)
       hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);

@@ -144,6 +144,16 @@ CASES = [
     ("softcap nan", dict(softcap=float("nan")), "gfx950", INVALID),
     ("lse misaligned", dict(lse=0x1c0002), "gfx950", INVALID),
     ("precision -1", dict(precision=-1), "gfx950", INVALID),
+    # in-launch merge sync words: 16 sequences x 1 merge group x 512 bytes
+    ("merge sync", dict(merge_sync=0x1e0000, merge_sync_size=16 * 512), "gfx950", OK),
+    ("merge sync too small", dict(merge_sync=0x1e0000, merge_sync_size=16 * 512 - 1), "gfx950", INVALID),
+    ("merge sync misaligned", dict(merge_sync=0x1e0080, merge_sync_size=1 << 20), "gfx950", INVALID),
+    ("merge sync, gqa 32", dict(num_q_heads=32, workspace_size=pfkv.workspace_bytes(16, 64, 32),
+                                merge_sync=0x1e0000, merge_sync_size=16 * 2 * 512 - 1), "gfx950", INVALID),
+    ("merge sync, 8 tokens", dict(max_q_len=8, total_q=128, workspace_size=pfkv.workspace_bytes(16, 128, 16),
+                                  merge_sync=0x1e0000, merge_sync_size=16 * 2 * 512), "gfx950", OK),
+    ("merge wait negative", dict(merge_wait_us=-1), "gfx950", OK),
+    ("merge wait too long", dict(merge_wait_us=100001), "gfx950", INVALID),
     ("mi300", {}, "gfx942:sramecc+:xnack-", UNSUPPORTED),
     ("gfx9500 lookalike", {}, "gfx9500", UNSUPPORTED),
 ]
@@ -178,6 +188,19 @@ def test_workspace_bytes(lib):
     assert pfkv.workspace_bytes(16, 64, 16) == 16 * 64 * 16 * (256 * 2 + 8)
     assert pfkv.workspace_bytes(0, 64, 16) == 0
     assert pfkv.workspace_bytes(64, 8, 32) == 64 * 8 * 32 * (256 * 2 + 8)
+
+
+def test_merge_sync_bytes(lib):
+    # 128 words per merge group, at most num_q_heads / 4 groups per sequence
+    assert pfkv.merge_sync_bytes(16, 16) == 16 * 4 * 512
+    assert pfkv.merge_sync_bytes(4, 32) == 4 * 8 * 512
+    assert pfkv.merge_sync_bytes(0, 16) == 0
+    # the bound covers every split that check_args accepts
+    for hq, hkv, qmax in ((16, 1, 4), (16, 1, 8), (32, 1, 8), (8, 1, 8), (4, 1, 8), (32, 8, 4)):
+        need = pfkv.merge_sync_bytes(3, hq)
+        a = _valid_args(num_seqs=3, total_q=3, num_q_heads=hq, num_kv_heads=hkv, max_q_len=qmax,
+                        workspace_size=pfkv.workspace_bytes(16, 3, hq), merge_sync=0x1e0000, merge_sync_size=need)
+        assert binding.check_args(a, "gfx950") == OK, (hq, hkv, qmax, binding.last_error())
 
 
 def test_stream_read_validation(lib):
