@@ -268,8 +268,14 @@ __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, in
         }
       }
       w = row_weights<false>(m, l, -__builtin_inff(), 0.f);
-      for (int s = sb; s < se; ++s)
-        acc += lane_value(w.coef, s) * __builtin_convertvector(buf[i * S + s][lane], f32x4);
+      // at most kBatch segments per part (S <= 64): their LDS reads go out together
+      f16x4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (sb + k < se) v[k] = buf[i * S + sb + k][lane];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (sb + k < se) acc += lane_value(w.coef, sb + k) * __builtin_convertvector(v[k], f32x4);
     }
     if constexpr (PARTS > 1) {
       partial[wave][lane] = acc;
