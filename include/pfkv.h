@@ -105,11 +105,11 @@ typedef struct pfkv_args {
  * call allows it: 16-bit arithmetic, head_dim 256, page_size >= 16, no balanced
  * segments, num_segments >= 2, a grid of at most one work-group per CU and o
  * partials under 2 GiB. Other calls run the two launches and leave merge_sync
- * untouched. The result is bit for bit that of the two launches. It pays where
- * a work-group has at most one row to merge (query heads per work-group x
- * q_len <= num_segments: decode, 64 segments of 4-token drafts; 1.4 us of 57
- * at 16 x 35000 decode) and costs up to about 1% where it has more (4-token
- * drafts at 16 segments).
+ * untouched. The result is bit for bit that of the two launches. Measured, it
+ * pays at decode (one query token, 16 query heads per work-group, 16
+ * segments: 1.2 us of 56 at 16 x 35000) and costs up to about 2% on the
+ * other verify shapes (4-token drafts: the merge's synchronization and loads
+ * take as long as the launch boundary and the reduce).
  * The work-groups of a (sequence, head group) count their arrivals in
  * merge_sync; once all have written their partials each merges a share of the
  * group's rows with the reduce's arithmetic. A work-group waits at most

@@ -298,7 +298,7 @@ __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, in
 // them; words 64-65 the 64-bit mask of shares handed to the last arrival.
 //
 // Ordering without cache maintenance: the partials are written with
-// device-scope stores (partial_store<true>), each wave waits for all of its
+// device-scope stores (partial_store), each wave waits for all of its
 // stores to complete (at the device's coherence point) before the work-group
 // counts its arrival, and the merge reads them with device-scope loads issued
 // only after the arrivals are seen. An agent-scope release or acquire fence
