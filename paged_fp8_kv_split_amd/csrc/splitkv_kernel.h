@@ -1500,6 +1500,7 @@ splitkv_main_kernel(MainParams p) {
     rp.num_q_heads = p.num_q_heads;
     rp.num_segments = p.num_segments;
     rp.head_dim = p.head_dim;
+    static_assert(merge::kMergeLdsBcast + 16 <= C::kLdsBytes, "the merge's LDS fits the kernel's allocation");
     uint32_t* sync = p.merge_sync + (int64_t)merge_group * kMergeSyncWords;
     const int S = p.num_segments;
     // the summation order of the segment reduce for S (waves per row there; S <= 64 here)
