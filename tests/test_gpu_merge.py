@@ -229,3 +229,35 @@ def test_calls_it_does_not_serve_leave_the_buffer():
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
     assert not sync.any()
+
+
+@pytest.mark.parametrize("wait_us", [0, 5])
+def test_correct_while_another_stream_holds_the_cus(wait_us):
+    """Merge calls on one stream while full-device calls run on another: the
+    merge's work-groups may then not all be resident at once, so waits can end
+    by the time limit (5 us makes that likely) and shares go to the last
+    arrival. Every result must still equal the two launches' bits."""
+    case = _case("contend", [3000, 1200, 517, 2049] * 4, [4, 3, 1, 2] * 4, 16, 1, seed=71)
+    busy = make_case(workload("prod"), "cpu").to(DEV)
+    sync = pfkv.merge_sync_buffer(16, 16, DEV)
+    ref = pfkv.verify_attn(*_args(case), num_segments=16)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [torch.zeros_like(case.q) for _ in range(6)]
+    ws = torch.empty(binding.workspace_bytes(16, case.q.shape[0], 16), dtype=torch.uint8, device=DEV)
+    busy_out = torch.empty_like(busy.q)
+    busy_ws = torch.empty(binding.workspace_bytes(16, busy.q.shape[0], 16), dtype=torch.uint8, device=DEV)
+    print(f"[merge] contention, wait_us={wait_us}", flush=True)
+    with torch.cuda.stream(sb):
+        for _ in range(8):
+            pfkv.verify_attn(*_args(busy), num_segments=16, out=busy_out, workspace=busy_ws, stream=sb)
+    with torch.cuda.stream(sa):
+        for o in outs:
+            pfkv.verify_attn(*_args(case), num_segments=16, out=o, workspace=ws, stream=sa, merge_sync=sync,
+                             merge_wait_us=wait_us)
+    torch.cuda.synchronize()
+    for k, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), k
+    arrivals, gen, handed = _state(sync, 16)
+    assert not arrivals.any() and not handed.any()
+    assert (gen == len(outs)).all(), gen
