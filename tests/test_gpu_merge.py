@@ -120,6 +120,16 @@ def test_matches_two_launches(name, ctx, q_lens, hq, hkv, segments, max_q_len):
     _compare(case, segments, sync, max_q_len=max_q_len)
 
 
+@pytest.mark.parametrize("segments", [2, 3, 5, 24, 40, 63])
+def test_uneven_shares(segments):
+    """Segment counts that do not divide the 64 rows of a group: several
+    passes per share (2, 3, 5: 32, 22 and 13 rows), uneven parts (24, 40) and
+    126 (row, segment) vectors gathered at once (63, the most a share holds)."""
+    case = _case(f"uneven{segments}", [5000, 3100, 977, 4096], [4, 4, 4, 4], 16, 1, seed=80 + segments)
+    sync = pfkv.merge_sync_buffer(4, 16, DEV)
+    _compare(case, segments, sync)
+
+
 def test_options():
     case = _case("opts", [3000, 1200, 517, 2049] * 4, [4, 3, 1, 2] * 4, 16, 1, seed=21)
     sync = pfkv.merge_sync_buffer(16, 16, DEV)
