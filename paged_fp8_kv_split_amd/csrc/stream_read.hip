@@ -1,5 +1,5 @@
 // Streaming-read microbenchmark kernels: the practical HBM read ceiling that the
-// verify-attention bandwidth is judged against (aiter PR #5190, Microbenchmark:
+// verify-attention bandwidth is measured against (aiter PR #5190, Microbenchmark:
 // a streaming-read microbenchmark sets the device's practical read ceiling).
 //
 // Every variant reads the buffer as 4 KiB blocks, each wave of 8 per work-group
