@@ -122,6 +122,76 @@ __device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int m
   return min(max(((__attribute__((address_space(4))) const int32_t*)seq_lens)[b], 0), max_seq_len);
 }
 
+// The balanced schedule, computed by each wave that needs it, every lane
+// getting the same result: lane l takes sequences c + l of chunks c = 0, 64, ...
+// with one vector load each, where a loop over the sequences would wait on one
+// scalar load after another (up to 3 us of the reduce at 8 sequences). Same
+// integer formulas, so the same schedule.
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) v += __shfl_xor(v, k, 64);
+  return v;
+}
+__device__ __forceinline__ int lane_span(const int32_t* seq_lens, int i, int num_seqs, int max_seq_len, int window_left) {
+  return i < num_seqs ? segment_span(min(max(seq_lens[i], 0), max_seq_len), window_left) : 0;
+}
+// sum over the sequences of segment_span
+__device__ __forceinline__ int64_t total_span(const int32_t* seq_lens, int num_seqs, int max_seq_len, int window_left) {
+  const int lane = threadIdx.x & 63;
+  int64_t acc = 0;
+  for (int c = 0; c < num_seqs; c += 64) acc += lane_span(seq_lens, c + lane, num_seqs, max_seq_len, window_left);
+  return wave_sum_i64(acc);
+}
+struct BalancedSlot {
+  int b, seg, count;   // b = -1: the slot is past the last sequence's segments
+};
+// Slot x: the first sequence b whose running sum of segment counts passes x,
+// its segment x - (slots of sequences before b) and its segment count.
+__device__ __forceinline__ BalancedSlot balanced_slot(int x, const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                                                      int window_left, int slots, int cap) {
+  const int lane = threadIdx.x & 63;
+  const int64_t total = total_span(seq_lens, num_seqs, max_seq_len, window_left);
+  int carry = 0;   // slots of the sequences of earlier chunks
+  for (int c = 0; c < num_seqs; c += 64) {
+    const int i = c + lane;
+    const int n = i < num_seqs ? segment_count(lane_span(seq_lens, i, num_seqs, max_seq_len, window_left), total, slots,
+                                               num_seqs, cap)
+                               : 0;
+    int pre = n;   // inclusive prefix over the chunk's lanes
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int y = __shfl_up(pre, k, 64);
+      if (lane >= k) pre += y;
+    }
+    const uint64_t hit = __ballot(i < num_seqs && x < carry + pre);
+    if (hit != 0) {
+      const int j = __builtin_ctzll(hit);
+      const int pj = __shfl(pre, j, 64), nj = __shfl(n, j, 64);
+      return BalancedSlot{c + j, x - (carry + pj - nj), nj};
+    }
+    carry += __shfl(pre, 63, 64);
+  }
+  return BalancedSlot{-1, 0, 0};
+}
+// Query token t: its sequence b (the first with cu[b] <= t < cu[b + 1], -1 if
+// none) and b's segment count.
+__device__ __forceinline__ BalancedSlot balanced_row(int t, const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                                     int num_seqs, int max_seq_len, int window_left, int slots, int cap) {
+  const int lane = threadIdx.x & 63;
+  const int64_t total = total_span(seq_lens, num_seqs, max_seq_len, window_left);
+  for (int c = 0; c < num_seqs; c += 64) {
+    const int i = c + lane;
+    const bool in = i < num_seqs && t >= cu_seqlens_q[i] && t < cu_seqlens_q[i + 1];
+    const uint64_t hit = __ballot(in);
+    if (hit != 0) {
+      const int j = __builtin_ctzll(hit);
+      const int span = __shfl(lane_span(seq_lens, i, num_seqs, max_seq_len, window_left), j, 64);
+      return BalancedSlot{c + j, 0, segment_count(span, total, slots, num_seqs, cap)};
+    }
+  }
+  return BalancedSlot{-1, 0, 0};
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);

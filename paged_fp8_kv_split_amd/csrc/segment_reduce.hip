@@ -30,20 +30,9 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   int S = p.num_segments;
   if (BAL && valid) {
     // the row's sequence and its segment count, as the main kernel scheduled them
-    const int t = (int)(row / p.num_q_heads);
-    const __attribute__((address_space(4))) int32_t* cu = (const __attribute__((address_space(4))) int32_t*)p.cu_seqlens_q;
-    int b = -1;
-    for (int i = 0; i < p.num_seqs; ++i)
-      if (t >= cu[i] && t < cu[i + 1]) {
-        b = i;
-        break;
-      }
-    if (b >= 0) {
-      int64_t total = 0;
-      for (int i = 0; i < p.num_seqs; ++i) total += segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left);
-      S = segment_count(segment_span(clamped_len(p.seq_lens, b, p.max_seq_len), p.window_left), total, p.num_slots,
-                        p.num_seqs, p.num_segments);
-    }
+    const BalancedSlot sl = balanced_row((int)(row / p.num_q_heads), p.cu_seqlens_q, p.seq_lens, p.num_seqs,
+                                         p.max_seq_len, p.window_left, p.num_slots, p.num_segments);
+    if (sl.b >= 0) S = __builtin_amdgcn_readfirstlane(sl.count);
   }
   merge::merge_row<PARTS>(p, row, valid, S, wave % PARTS, wave, lane, partial);
 }

@@ -1417,21 +1417,11 @@ splitkv_main_kernel(MainParams p) {
   if constexpr (BAL) {
     // slot blockIdx.x -> (sequence, segment) by the balanced schedule; idle
     // slots past the last sequence's segments return before any barrier
-    int64_t total = 0;
-    for (int i = 0; i < p.num_seqs; ++i) total += segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left);
-    int acc = 0;
-    geo.b = -1;
-    for (int i = 0; i < p.num_seqs; ++i) {
-      const int n_i = segment_count(segment_span(clamped_len(p.seq_lens, i, p.max_seq_len), p.window_left), total,
-                                    (int)gridDim.x, p.num_seqs, p.num_segments);
-      if ((int)blockIdx.x < acc + n_i) {
-        geo.b = i;
-        geo.seg = blockIdx.x - acc;
-        seg_count = n_i;
-        break;
-      }
-      acc += n_i;
-    }
+    const BalancedSlot sl = balanced_slot((int)blockIdx.x, p.seq_lens, p.num_seqs, p.max_seq_len, p.window_left,
+                                          (int)gridDim.x, p.num_segments);
+    geo.b = __builtin_amdgcn_readfirstlane(sl.b);
+    geo.seg = __builtin_amdgcn_readfirstlane(sl.seg);
+    seg_count = __builtin_amdgcn_readfirstlane(sl.count);
     if (geo.b < 0) return;
   }
   geo.h = wg_z / p.q_split;
