@@ -79,7 +79,7 @@ def kernel_source_digest():
     and the 16-bit instantiation) with comments and blank lines removed, so
     that a change to the code changes it and a change to a comment does not."""
     h = hashlib.sha256()
-    for name in ("splitkv_kernel.h", "segment_merge.h", "splitkv_main.hip", "pfkv_internal.h"):
+    for name in ("splitkv_kernel.h", "segment_merge.h", "splitkv_main.hip", "splitkv_main_rm.hip", "pfkv_internal.h"):
         with open(os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", name)) as f:
             text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
         for line in text.splitlines():

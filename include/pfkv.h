@@ -273,7 +273,10 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
  * the segment's softmax-weighted mean of V (without v_descale, 0 for a segment
  * with no visible key; at head_dim 128 the first 128 of each row), then fp32 (m, l)[S][total_q][num_q_heads], m the
  * segment's reference max of the scores in log2 units (-inf when empty) and
- * l the sum of 2^(score - m) over its keys.
+ * l the sum of 2^(score - m) over its keys. Above 16 segments in the 16-bit
+ * mode at head_dim 256 with pages of 16 tokens or more, both arrays are
+ * row-major instead, o[total_q][num_q_heads][S][256] and (m, l)[total_q]
+ * [num_q_heads][S], so that a row's partials are contiguous for the reduce.
  */
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads);
 

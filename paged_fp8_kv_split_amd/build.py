@@ -23,7 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpfkv.so")
 
-KERNEL_SOURCES = ["splitkv_main.hip", "splitkv_main_fp8p.hip", "splitkv_main_fp8.hip", "splitkv_main_hd128.hip",
+KERNEL_SOURCES = ["splitkv_main.hip", "splitkv_main_rm.hip", "splitkv_main_fp8p.hip", "splitkv_main_fp8.hip",
+                  "splitkv_main_hd128.hip",
                   "segment_reduce.hip",
                   "stream_read.hip", "debug_check.hip", "prefill.hip", "noalloc.hip"]
 SOURCES = ["pfkv_host.cpp", *KERNEL_SOURCES]

@@ -398,6 +398,11 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bo
     m.num_slots = std::max(a->num_seqs, std::max(1, d.num_cus / per_slot));
   }
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
+  // row-major partials above 16 segments, where that instantiation exists
+  m.ws_row_major = a->num_segments > pfkv::kRowMajorAbove && a->precision == PFKV_PRECISION_16BIT &&
+                           a->head_dim == 256 && a->page_size >= 16
+                       ? 1
+                       : 0;
   m.merge_sync = nullptr;
   if (a->merge_sync != nullptr) {
     st = check_device_pointer(a->merge_sync, device, "merge_sync");
@@ -433,6 +438,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bo
   rp->max_seq_len = m.max_seq_len;
   rp->seq_lens = a->seq_lens;
   rp->cu_seqlens_q = a->cu_seqlens_q;
+  rp->ws_row_major = m.ws_row_major;
   (void)group;
   return PFKV_OK;
 }

@@ -22,7 +22,28 @@ constexpr int kMaxBalancedSegments = 128;   // the cap per sequence with balance
 //                            (head dim 128: the first 128 of each row's 256)
 //   ml [S][T][Hq][2]   fp32  (m, l): reference max in log2 units and l = sum p
 // so that segment s contributes  2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.
+// Above 16 segments (16-bit arithmetic, head dim 256, pages of 16 or more) the
+// two arrays are row-major instead, [T][Hq][S][256] and [T][Hq][S][2]
+// (ws_row_major), so that a row's partials are one contiguous run for the merge
+// (ws_slot). The layout is a template argument of the kernels: a runtime choice
+// costs the segment-major stores their folded address offsets.
 constexpr int kPartialBytes = kHeadDim * 2 + 2 * 4;   // workspace bytes per (segment, token, head)
+constexpr int kRowMajorAbove = 16;                   // segments above which the partials are row-major
+
+// Slot of (row, segment s) in the o and ml arrays, in units of one row's
+// partial (256 fp16, or one (m, l) pair); RM: row-major.
+template <bool RM>
+__host__ __device__ __forceinline__ int64_t ws_slot(int64_t row, int s, int64_t rows_total, int S) {
+  if constexpr (RM) return row * S + s;
+  else return (int64_t)s * rows_total + row;
+}
+// The same for the row of query token q0 + i and query head h0 + g (of T and
+// Hq), each sum taken in 64 bits.
+template <bool RM>
+__host__ __device__ __forceinline__ int64_t ws_slot_tq(int q0, int i, int h0, int g, int seg, int T, int Hq, int S) {
+  if constexpr (RM) return (((int64_t)q0 + i) * Hq + h0 + g) * S + seg;
+  else return ((int64_t)seg * T + q0 + i) * Hq + h0 + g;
+}
 
 // In-launch merge (opt-in): 32-bit sync words per merge group, a (sequence,
 // blockIdx.z) pair of the main grid: [0] arrivals (bits 0-7) and generation
@@ -79,6 +100,7 @@ struct MainParams {
   // most merge_wait_ticks ticks of the 100 MHz clock for the rest of its group
   uint32_t* merge_sync;
   uint32_t merge_wait_ticks;
+  int32_t ws_row_major;        // partials row-major (selects the RM instantiations), see ws_slot
 };
 
 struct ReduceParams {
@@ -96,6 +118,7 @@ struct ReduceParams {
   int32_t balance, num_slots, num_seqs, window_left, max_seq_len;
   const int32_t* seq_lens;
   const int32_t* cu_seqlens_q;
+  int32_t ws_row_major;        // as MainParams
 };
 
 // Pages (16-token blocks) that the segments of a sequence of L keys split:
@@ -240,6 +263,8 @@ int set_error(int status, const char* msg);
 hipError_t launch_splitkv_main_fp8p(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_splitkv_main_fp8(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_splitkv_main_hd128(const MainParams& p, int group, hipStream_t stream);
+// the 16-bit mode at head dim 256 with row-major partials (pages of 16 or more)
+hipError_t launch_splitkv_main_rm(const MainParams& p, int group, hipStream_t stream);
 hipError_t launch_precondition_check(const CheckParams& p, int32_t* status, hipStream_t stream);
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

@@ -112,7 +112,7 @@ __device__ __forceinline__ void finish_row(const ReduceParams& p, int64_t row, f
     p.lse[hq * p.total_q + t] = den > 0.f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
-template <int PARTS>
+template <int PARTS, bool RM>
 __device__ __forceinline__ void merge_row(const ReduceParams& p, int64_t row, bool valid, int S, int part, int wave,
                                           int lane, f32x4 (*partial)[64]) {
   constexpr bool kWide = PARTS == 8;   // up to 128 segments: two (m, l) per lane
@@ -126,8 +126,9 @@ __device__ __forceinline__ void merge_row(const ReduceParams& p, int64_t row, bo
   RowWeights w = {-__builtin_inff(), 0.f, 0.f, 0.f};
   if (valid) {
     // the o loads of the first segments go out before (m, l) is known
-    const _Float16* o = (const _Float16*)p.ws_o + row * kHeadDim + 4 * lane;
-    const int64_t seg_stride = rows_total * kHeadDim;
+    const _Float16* o =
+        (const _Float16*)p.ws_o + ws_slot<RM>(row, 0, rows_total, p.num_segments) * kHeadDim + 4 * lane;
+    const int64_t seg_stride = (RM ? 1 : rows_total) * kHeadDim;
     f16x4 a[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
@@ -135,7 +136,7 @@ __device__ __forceinline__ void merge_row(const ReduceParams& p, int64_t row, bo
 
     float m = -__builtin_inff(), l = 0.f;
     if (lane < S) {
-      const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
+      const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + ws_slot<RM>(row, lane, rows_total, p.num_segments) * 2));
       m = v[0];
       l = v[1];
     }
@@ -144,7 +145,7 @@ __device__ __forceinline__ void merge_row(const ReduceParams& p, int64_t row, bo
     float m2 = -__builtin_inff(), l2 = 0.f;
     if constexpr (kWide) {
       if (lane + 64 < S) {
-        const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + ((lane + 64) * rows_total + row) * 2));
+        const f32x2 v = __builtin_nontemporal_load((const f32x2*)(p.ws_ml + ws_slot<RM>(row, lane + 64, rows_total, p.num_segments) * 2));
         m2 = v[0];
         l2 = v[1];
       }
@@ -200,7 +201,7 @@ constexpr int kMergeLdsBcast = kMergeLdsPartial + 8 * 64 * 16;
 // Then PARTS waves per row sum the row's segments exactly as the segment
 // reduce does for S (each part's segments in order, then the parts in order),
 // so that the bits equal the reduce's.
-template <int PARTS, int G>
+template <int PARTS, int G, bool RM>
 __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, int S, int R, int q0, int hbase,
                                             int wave, int lane, uint8_t* lds, float vd) {
   const int per = (R + S - 1) / S;
@@ -232,14 +233,14 @@ __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, in
     a[k] = f16x8{};
     if (2 * (wave + 8 * k) < tasks && t < tasks && 8 * hl < p.head_dim)
       a[k] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                           o_rsrc, (int)(((s * rows_total + row_of(i)) * kHeadDim + 8 * hl) * 2), 0,
+                                           o_rsrc, (int)((ws_slot<RM>(row_of(i), s, rows_total, p.num_segments) * kHeadDim + 8 * hl) * 2), 0,
                                            kSc1));
   }
   // (m, l) of this wave's row in the first pass go out with them
   const int prow = wave / PARTS, part = wave % PARTS;
   float m = -__builtin_inff(), l = 0.f;
   if (prow < n && lane < S) {
-    const f32x2 v = coherent_load((const f32x2*)(p.ws_ml + (lane * rows_total + row_of(prow)) * 2));
+    const f32x2 v = coherent_load((const f32x2*)(p.ws_ml + ws_slot<RM>(row_of(prow), lane, rows_total, p.num_segments) * 2));
     m = v[0];
     l = v[1];
   }
@@ -262,7 +263,7 @@ __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, in
         m = -__builtin_inff();
         l = 0.f;
         if (lane < S) {
-          const f32x2 v = coherent_load((const f32x2*)(p.ws_ml + (lane * rows_total + row) * 2));
+          const f32x2 v = coherent_load((const f32x2*)(p.ws_ml + ws_slot<RM>(row, lane, rows_total, p.num_segments) * 2));
           m = v[0];
           l = v[1];
         }
@@ -320,7 +321,7 @@ __device__ __forceinline__ void merge_share(const ReduceParams& p, int share, in
 // writes the same bits).
 enum : int { kMergeOwn = 0, kMergeLast = 1, kMergeLeave = 2 };
 
-template <int PARTS, int G>
+template <int PARTS, int G, bool RM>
 __device__ __forceinline__ void merge_in_launch(const ReduceParams& p, uint32_t* sync, uint32_t wait_ticks, int share,
                                                 int S, int R, int q0, int hbase, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -367,7 +368,7 @@ __device__ __forceinline__ void merge_in_launch(const ReduceParams& p, uint32_t*
   __syncthreads();
   const int role = (int)bcast[0];
   if (role == kMergeLeave) return;
-  merge_share<PARTS, G>(p, share, S, R, q0, hbase, wave, lane, smem, vd);
+  merge_share<PARTS, G, RM>(p, share, S, R, q0, hbase, wave, lane, smem, vd);
   if (role != kMergeLast) return;
   // the last arrival: the shares handed to it, taken once its addition to the
   // word has been performed (it was issued before the merge above; the wait
@@ -383,7 +384,7 @@ __device__ __forceinline__ void merge_in_launch(const ReduceParams& p, uint32_t*
   while (rescue != 0) {
     const int s = __builtin_ctzll(rescue);
     rescue &= rescue - 1;
-    merge_share<PARTS, G>(p, s, S, R, q0, hbase, wave, lane, smem, vd);
+    merge_share<PARTS, G, RM>(p, s, S, R, q0, hbase, wave, lane, smem, vd);
   }
 }
 

@@ -17,7 +17,7 @@ namespace {
 // PARTS waves merge one row (merge::merge_row). With many segments and few
 // rows (4 sequences x 64 segments: 256 rows) one wave per row would load its
 // segments in several dependent batches on a few CUs.
-template <int PARTS, bool BAL>
+template <int PARTS, bool BAL, bool RM>
 __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
   constexpr int kRowsPerWg = 8 / PARTS;
   __shared__ merge::f32x4 partial[PARTS > 1 ? 8 : 1][64];
@@ -34,7 +34,18 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
                                          p.max_seq_len, p.window_left, p.num_slots, p.num_segments);
     if (sl.b >= 0) S = __builtin_amdgcn_readfirstlane(sl.count);
   }
-  merge::merge_row<PARTS>(p, row, valid, S, wave % PARTS, wave, lane, partial);
+  merge::merge_row<PARTS, RM>(p, row, valid, S, wave % PARTS, wave, lane, partial);
+}
+
+template <int PARTS>
+void launch_rows(const ReduceParams& p, dim3 grid, hipStream_t stream) {
+  if (p.balance) {
+    if (p.ws_row_major) hipLaunchKernelGGL((segment_reduce_kernel<PARTS, true, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<PARTS, true, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    if (p.ws_row_major) hipLaunchKernelGGL((segment_reduce_kernel<PARTS, false, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<PARTS, false, false>), grid, dim3(512), 0, stream, p);
+  }
 }
 
 }  // namespace
@@ -42,22 +53,24 @@ __global__ void __launch_bounds__(512) segment_reduce_kernel(ReduceParams p) {
 hipError_t launch_segment_reduce(const ReduceParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   // waves per row: one up to 16 segments (a single batch of loads), else 2 or 4
-  // (balanced segments: a separate instantiation that finds each row's count)
+  // (balanced segments: a separate instantiation that finds each row's count);
+  // row-major partials come only above 16 segments
   if (p.num_segments <= 16) {
+    if (p.ws_row_major) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((rows + 7) / 8));
-    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<1, true>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((segment_reduce_kernel<1, false>), grid, dim3(512), 0, stream, p);
+    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<1, true, false>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<1, false, false>), grid, dim3(512), 0, stream, p);
   } else if (p.num_segments <= 32) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<2, true>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((segment_reduce_kernel<2, false>), grid, dim3(512), 0, stream, p);
+    launch_rows<2>(p, grid, stream);
   } else if (p.num_segments <= 64) {
     const dim3 grid((unsigned)((rows + 1) / 2));
-    if (p.balance) hipLaunchKernelGGL((segment_reduce_kernel<4, true>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((segment_reduce_kernel<4, false>), grid, dim3(512), 0, stream, p);
+    launch_rows<4>(p, grid, stream);
   } else {
     // above 64 segments (balanced caps only): eight waves per row
-    hipLaunchKernelGGL((segment_reduce_kernel<8, true>), dim3((unsigned)rows), dim3(512), 0, stream, p);
+    if (!p.balance) return hipErrorInvalidValue;
+    if (p.ws_row_major) hipLaunchKernelGGL((segment_reduce_kernel<8, true, true>), dim3((unsigned)rows), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((segment_reduce_kernel<8, true, false>), dim3((unsigned)rows), dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }

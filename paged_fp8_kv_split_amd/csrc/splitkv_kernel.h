@@ -475,7 +475,7 @@ struct PageStream {
 // 512 threads: fp16 o rows to the workspace (row stride kHeadDim) with 16-byte
 // streaming stores, or, with a single segment, the final bf16 rows to out with
 // 8-byte stores (out rows are 8-byte aligned).
-template <int G, int D>
+template <int G, int D, bool RM>
 __device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, const uint8_t* obuf) {
   constexpr int kQuads = D / 4, kOcts = D / 8;   // 8-byte and 16-byte pieces of a row
   if (p.direct) {
@@ -491,7 +491,7 @@ __device__ __forceinline__ void store_rows(const MainParams& p, const Geo& geo, 
   for (int idx = threadIdx.x; idx < geo.rows * kOcts; idx += kThreads) {
     const int row = idx / kOcts, c = idx % kOcts;
     const int i = row / G, gg = row - (row / G) * G;
-    uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + geo.q0 + i) * Hq + geo.h * G + gg) * kHeadDim + 8 * c;
+    uint16_t* dst = p.ws_o + ws_slot_tq<RM>(geo.q0, i, geo.h * G, gg, geo.seg, T, Hq, p.num_segments) * kHeadDim + 8 * c;
     __builtin_nontemporal_store(*(const u32x4*)(obuf + row * (2 * D) + 16 * c), (u32x4*)dst);
   }
 }
@@ -529,7 +529,7 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // Q is quantised to e4m3 with a power-of-two scale per 32 dims and S^T runs on
 // the scaled fp8 MFMA; with F8P, P is rounded to e4m3 with a power-of-two
 // scale per (row, 32 keys).
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool RM>
 __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G, D>;
   using Dm = Dim<D>;
@@ -975,7 +975,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
           p.lse[(int64_t)(h * G + gg) * T + q0 + i] =
               den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
         } else {
-          float* dst = p.ws_ml + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * 2;
+          float* dst = p.ws_ml + ws_slot_tq<RM>(q0, i, h * G, gg, geo.seg, T, Hq, p.num_segments) * 2;
           partial_store(m_ref[rb], dst);
           partial_store(l, dst + 1);
         }
@@ -984,7 +984,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
   }
   if constexpr (F8P) {
     lds_barrier();   // o staged
-    store_rows<G, D>(p, geo, smem + C::kOffObuf);
+    store_rows<G, D, RM>(p, geo, smem + C::kOffObuf);
   }
 }
 
@@ -992,7 +992,7 @@ __device__ __forceinline__ void score_wave(const MainParams& p, const Geo& geo, 
 // NRB row blocks; stages its slice of the segment's normalised output o. With
 // F8, O += P V runs on the 32x32x64 fp8 MFMA over 32-row tiles, P and V as
 // e4m3 bytes.
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool RM>
 __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uint8_t* smem) {
   using C = Cfg<G, D>;
   using Dm = Dim<D>;
@@ -1292,7 +1292,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
         }
       }
     lds_barrier();
-    store_rows<G, D>(p, geo, smem + C::kOffObuf);
+    store_rows<G, D, RM>(p, geo, smem + C::kOffObuf);
   } else {
     // o = acc / l (0 with no visible key); a single segment writes out = vd o.
     // Lane (g, n) holds dims kVDims v + 16 db + n of rows 16 rb + 4 g + r. A
@@ -1350,7 +1350,7 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
               else
                 *(unsigned*)dst = wd[0];
             } else {
-              uint16_t* dst = p.ws_o + (((int64_t)geo.seg * T + q0 + i) * Hq + h * G + gg) * kHeadDim + dim0;
+              uint16_t* dst = p.ws_o + ws_slot_tq<RM>(q0, i, h * G, gg, geo.seg, T, Hq, p.num_segments) * kHeadDim + dim0;
               if constexpr (NDB == 4)
                 partial_store(u32x2{wd[0], wd[1]}, (u32x2*)dst);
               else
@@ -1366,17 +1366,17 @@ __device__ __forceinline__ void pv_wave(const MainParams& p, const Geo& geo, uin
   }
 }
 
-template <int G, int NRB, int MODE, bool TOK, int D>
+template <int G, int NRB, int MODE, bool TOK, int D, bool RM>
 __device__ __forceinline__ void verify_segment(const MainParams& p, const Geo& geo, uint8_t* smem) {
   if (threadIdx.x < 64 * kPagesPerStep)
-    score_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
+    score_wave<G, NRB, MODE, TOK, D, RM>(p, geo, smem);
   else
-    pv_wave<G, NRB, MODE, TOK, D>(p, geo, smem);
+    pv_wave<G, NRB, MODE, TOK, D, RM>(p, geo, smem);
 }
 
 // TOK: the cache has one-token pages; D: head dim; MERGE: the in-launch merge
-// (merge::merge_in_launch) follows the segment
-template <int G, int MODE, bool TOK, int D, bool BAL, bool MERGE = false>
+// (merge::merge_in_launch) follows the segment; RM: row-major partials
+template <int G, int MODE, bool TOK, int D, bool BAL, bool MERGE = false, bool RM = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 splitkv_main_kernel(MainParams p) {
   using C = Cfg<G, D>;
@@ -1457,23 +1457,23 @@ splitkv_main_kernel(MainParams p) {
   const int merge_group = geo.b * (int)gridDim.z + wg_z;
   if constexpr (G == 16) {
     switch (nrb) {
-      case 1: verify_segment<16, 1, MODE, TOK, D>(p, geo, smem); break;
-      case 2: verify_segment<16, 2, MODE, TOK, D>(p, geo, smem); break;
-      case 3: verify_segment<16, 3, MODE, TOK, D>(p, geo, smem); break;
-      default: verify_segment<16, 4, MODE, TOK, D>(p, geo, smem); break;
+      case 1: verify_segment<16, 1, MODE, TOK, D, RM>(p, geo, smem); break;
+      case 2: verify_segment<16, 2, MODE, TOK, D, RM>(p, geo, smem); break;
+      case 3: verify_segment<16, 3, MODE, TOK, D, RM>(p, geo, smem); break;
+      default: verify_segment<16, 4, MODE, TOK, D, RM>(p, geo, smem); break;
     }
   } else if constexpr (G == 8) {
     switch (nrb) {
-      case 1: verify_segment<8, 1, MODE, TOK, D>(p, geo, smem); break;
-      case 2: verify_segment<8, 2, MODE, TOK, D>(p, geo, smem); break;
-      case 3: verify_segment<8, 3, MODE, TOK, D>(p, geo, smem); break;
-      default: verify_segment<8, 4, MODE, TOK, D>(p, geo, smem); break;
+      case 1: verify_segment<8, 1, MODE, TOK, D, RM>(p, geo, smem); break;
+      case 2: verify_segment<8, 2, MODE, TOK, D, RM>(p, geo, smem); break;
+      case 3: verify_segment<8, 3, MODE, TOK, D, RM>(p, geo, smem); break;
+      default: verify_segment<8, 4, MODE, TOK, D, RM>(p, geo, smem); break;
     }
   } else {
     if (nrb == 1)
-      verify_segment<4, 1, MODE, TOK, D>(p, geo, smem);
+      verify_segment<4, 1, MODE, TOK, D, RM>(p, geo, smem);
     else
-      verify_segment<4, 2, MODE, TOK, D>(p, geo, smem);
+      verify_segment<4, 2, MODE, TOK, D, RM>(p, geo, smem);
   }
   if constexpr (MERGE) {
     // the segment reduce's per-row arithmetic, on this group's rows
@@ -1490,43 +1490,44 @@ splitkv_main_kernel(MainParams p) {
     rp.num_q_heads = p.num_q_heads;
     rp.num_segments = p.num_segments;
     rp.head_dim = p.head_dim;
+    rp.ws_row_major = RM;
     static_assert(merge::kMergeLdsBcast + 16 <= C::kLdsBytes, "the merge's LDS fits the kernel's allocation");
     uint32_t* sync = p.merge_sync + (int64_t)merge_group * kMergeSyncWords;
     const int S = p.num_segments;
     // the summation order of the segment reduce for S (waves per row there; S <= 64 here)
-    if (S <= 16)
-      merge::merge_in_launch<1, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
+    if (!RM && S <= 16)
+      merge::merge_in_launch<1, G, RM>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
     else if (S <= 32)
-      merge::merge_in_launch<2, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
+      merge::merge_in_launch<2, G, RM>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
     else
-      merge::merge_in_launch<4, G>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
+      merge::merge_in_launch<4, G, RM>(rp, sync, p.merge_wait_ticks, geo.seg, S, geo.rows, geo.q0, geo.h * G, smem);
   }
 }
 
-// TOK: one-token cache pages; D: head dim
-template <int MODE, bool TOK, int D>
+// TOK: one-token cache pages; D: head dim; RM: row-major partials
+template <int MODE, bool TOK, int D, bool RM = false>
 hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
   // balanced: p.num_slots slots along x (see MainParams), else segments x sequences
   const dim3 grid(p.balance ? p.num_slots : p.num_segments, p.balance ? 1 : p.num_seqs,
                   p.num_kv_heads * p.kv_split * p.q_split);
   if (p.balance) {
     if (group == 16)
-      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, true, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else if (group == 8)
-      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, true, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else if (group == 4)
-      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, true, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else
       return hipErrorInvalidValue;
   } else if (p.merge_sync != nullptr) {
     // the in-launch merge: 16-bit arithmetic, head dim 256, pages of 16 or more
     if constexpr (MODE == kMode16 && !TOK && D == 256) {
       if (group == 16)
-        hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false, true, RM>), grid, dim3(kThreads), 0, stream, p);
       else if (group == 8)
-        hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false, true, RM>), grid, dim3(kThreads), 0, stream, p);
       else if (group == 4)
-        hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false, true, RM>), grid, dim3(kThreads), 0, stream, p);
       else
         return hipErrorInvalidValue;
     } else {
@@ -1534,11 +1535,11 @@ hipError_t launch_shape(const MainParams& p, int group, hipStream_t stream) {
     }
   } else {
     if (group == 16)
-      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<16, MODE, TOK, D, false, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else if (group == 8)
-      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<8, MODE, TOK, D, false, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else if (group == 4)
-      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((splitkv_main_kernel<4, MODE, TOK, D, false, false, RM>), grid, dim3(kThreads), 0, stream, p);
     else
       return hipErrorInvalidValue;
   }

@@ -6,6 +6,11 @@ namespace pfkv {
 
 hipError_t launch_splitkv_main(const MainParams& p, int group, hipStream_t stream) {
   if (p.kv_split != 1 && !(p.kv_split == 2 && group == 16)) return hipErrorInvalidValue;
+  if (p.ws_row_major) {
+    // instantiated only where row-major partials are used
+    if (p.precision != kMode16 || p.head_dim != 256 || p.token_pages) return hipErrorInvalidValue;
+    return launch_splitkv_main_rm(p, group, stream);
+  }
   if (p.head_dim == 128) return launch_splitkv_main_hd128(p, group, stream);
   if (p.head_dim != 256) return hipErrorInvalidValue;
   switch (p.precision) {

@@ -112,18 +112,26 @@ def test_full_size_all_rows(name):
 
 
 # ------------------------------------------------------------------ workspace partials
-def test_segment_partials_match_oracle():
+@pytest.mark.parametrize("S", [8, 24])
+def test_segment_partials_match_oracle(S):
     w = Workload(name="p", ctx=(3000, 300, 20), q_lens=(4, 3, 1), num_q_heads=16, num_kv_heads=1,
-                 num_segments=8, seed=33)
+                 num_segments=S, seed=33)
     case = make_case(w, "cpu").to(DEV)
-    S, T, Hq = 8, w.total_q, w.num_q_heads
+    T, Hq = w.total_q, w.num_q_heads
     ws = torch.zeros(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device=DEV)
     run(case, num_segments=S, workspace=ws)
     torch.cuda.synchronize()
-    # layout: fp16 o[S][T][Hq][256], then fp32 (m, l)[S][T][Hq]
+    # layout: fp16 o[S][T][Hq][256], then fp32 (m, l)[S][T][Hq]; above 16
+    # segments row-major, o[T][Hq][S][256] and (m, l)[T][Hq][S]
     n_o = S * T * Hq * 256 * 2
-    o16 = ws[:n_o].view(torch.float16).view(S, T, Hq, 256).double().cpu().numpy()
-    ml = ws[n_o:n_o + S * T * Hq * 8].view(torch.float32).view(S, T, Hq, 2).double().cpu().numpy()
+    o16 = ws[:n_o].view(torch.float16)
+    ml = ws[n_o:n_o + S * T * Hq * 8].view(torch.float32)
+    if S > 16:
+        o16 = o16.view(T, Hq, S, 256).permute(2, 0, 1, 3)
+        ml = ml.view(T, Hq, S, 2).permute(2, 0, 1, 3)
+    else:
+        o16, ml = o16.view(S, T, Hq, 256), ml.view(S, T, Hq, 2)
+    o16, ml = o16.double().cpu().numpy(), ml.double().cpu().numpy()
     lse2, o = oracle.segment_partials(**case.to("cpu").host_arrays(), num_segments=S)
     m, l = ml[..., 0], ml[..., 1]
     empty = np.isneginf(lse2)
@@ -135,6 +143,37 @@ def test_segment_partials_match_oracle():
     seg_out = o16[~empty] * vd
     sigma = o[~empty].std()
     assert np.max(np.abs(seg_out - o[~empty])) <= 0.05 * sigma
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_partials_layout_by_mode(precision):
+    """Row-major partials only where documented (16-bit mode, head dim 256,
+    pages of 16 or more, above 16 segments). At 24 segments the three
+    sequences fill 24, 19 and 2 of them, so read in the wrong layout the
+    empty-segment pattern and the segment log-sum-exps would not match the
+    oracle's. The e4m3-P mode's l sums e4m3-rounded weights (relative error at
+    most 2^-4 each), hence its looser bound, log2(1 + 2^-4) plus rounding."""
+    w = Workload(name="p", ctx=(3000, 300, 20), q_lens=(4, 3, 1), num_q_heads=16, num_kv_heads=1,
+                 num_segments=24, seed=34)
+    case = make_case(w, "cpu").to(DEV)
+    S, T, Hq = 24, w.total_q, w.num_q_heads
+    ws = torch.zeros(pfkv.workspace_bytes(S, T, Hq), dtype=torch.uint8, device=DEV)
+    run(case, num_segments=S, workspace=ws, precision=precision)
+    torch.cuda.synchronize()
+    ml = ws[S * T * Hq * 512:S * T * Hq * 520].view(torch.float32)
+    if precision == 0:
+        ml = ml.view(T, Hq, S, 2).permute(2, 0, 1, 3)
+    else:
+        ml = ml.view(S, T, Hq, 2)
+    ml = ml.double().cpu().numpy()
+    lse2, _ = oracle.segment_partials(**case.to("cpu").host_arrays(), num_segments=S)
+    m, l = ml[..., 0], ml[..., 1]
+    empty = np.isneginf(lse2)
+    assert empty.any() and (~empty).any()
+    assert np.array_equal(empty, l == 0) and np.all(np.isneginf(m[empty]))
+    got = m[~empty] + np.log2(l[~empty])
+    tol = 2e-3 if precision == 0 else math.log2(1 + 2.0 ** -4) + 2e-3
+    assert np.max(np.abs(got - lse2[~empty])) < tol
 
 
 # ------------------------------------------------------------------ bit-exact invariants
