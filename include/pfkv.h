@@ -276,9 +276,20 @@ int pfkv_num_segments(int num_cus, int num_seqs, int num_kv_heads);
  * l the sum of 2^(score - m) over its keys. Above 16 segments in the 16-bit
  * mode at head_dim 256 with pages of 16 tokens or more, both arrays are
  * row-major instead, o[total_q][num_q_heads][S][256] and (m, l)[total_q]
- * [num_q_heads][S], so that a row's partials are contiguous for the reduce.
+ * [num_q_heads][S], so that a row's partials are contiguous for the reduce
+ * (pfkv_partials_row_major).
  */
 uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads);
+
+/*
+ * 1 when a call with these arguments leaves its workspace partials row-major
+ * (layout above), 0 when segment-major; the same test the call itself makes,
+ * for callers that read the partials (for instance to merge them with those of
+ * another chunk of keys, the split-softmax merge of aiter PR #5190,
+ * Modifications). precision is a PFKV_PRECISION_* value. Pure: no device is
+ * touched and any values are accepted (0 for the ones a call would refuse).
+ */
+int pfkv_partials_row_major(int precision, int head_dim, int page_size, int num_segments);
 
 /*
  * Text of the most recent failure on this host thread ("" if none), naming the

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     merge_sync_buffer,
     merge_sync_bytes,
     num_segments,
+    partials_row_major,
     prefill_attn,
     set_debug,
     stream_read,

@@ -140,6 +140,8 @@ def load_library():
     lib.pfkv_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.pfkv_workspace_bytes.restype = ctypes.c_uint64
     lib.pfkv_merge_sync_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.pfkv_partials_row_major.argtypes = [ctypes.c_int] * 4
+    lib.pfkv_partials_row_major.restype = ctypes.c_int
     lib.pfkv_merge_sync_bytes.restype = ctypes.c_uint64
     lib.pfkv_last_error.argtypes = []
     lib.pfkv_last_error.restype = ctypes.c_char_p
@@ -192,6 +194,13 @@ def num_segments(num_cus: int, num_seqs: int, num_kv_heads: int) -> int:
 
 def workspace_bytes(num_segments_: int, total_q: int, num_q_heads: int) -> int:
     return int(load_library().pfkv_workspace_bytes(int(num_segments_), int(total_q), int(num_q_heads)))
+
+
+def partials_row_major(precision: int, head_dim: int, page_size: int, num_segments_: int) -> bool:
+    """Whether a call with these arguments leaves its workspace partials
+    row-major ([T][Hq][S][...]) rather than segment-major ([S][T][Hq][...])."""
+    return bool(load_library().pfkv_partials_row_major(int(precision), int(head_dim), int(page_size),
+                                                       int(num_segments_)))
 
 
 def merge_sync_bytes(num_seqs: int, num_q_heads: int) -> int:

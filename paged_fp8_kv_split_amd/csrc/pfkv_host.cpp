@@ -199,6 +199,16 @@ uint64_t pfkv_workspace_bytes(int num_segments, int total_q, int num_q_heads) {
   return (uint64_t)num_segments * (uint64_t)total_q * (uint64_t)num_q_heads * pfkv::kPartialBytes;
 }
 
+int pfkv_partials_row_major(int precision, int head_dim, int page_size, int num_segments) {
+  // the instantiations that write row-major partials: 16-bit arithmetic, head
+  // dim 256, pages of 16 tokens or more
+  const bool pages = page_size == 16 || page_size == 32 || page_size == 64;
+  return precision == PFKV_PRECISION_16BIT && head_dim == 256 && pages && num_segments > pfkv::kRowMajorAbove &&
+                 num_segments <= pfkv::kMaxBalancedSegments
+             ? 1
+             : 0;
+}
+
 uint64_t pfkv_merge_sync_bytes(int num_seqs, int num_q_heads) {
   // merge groups per sequence: num_kv_heads * kv_split * q_split <= num_q_heads / 4
   if (num_seqs <= 0 || num_q_heads <= 0) return 0;
@@ -398,11 +408,7 @@ int prepare(const pfkv_args* a, pfkv::MainParams* mp, pfkv::ReduceParams* rp, bo
     m.num_slots = std::max(a->num_seqs, std::max(1, d.num_cus / per_slot));
   }
   m.score_scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634073599);
-  // row-major partials above 16 segments, where that instantiation exists
-  m.ws_row_major = a->num_segments > pfkv::kRowMajorAbove && a->precision == PFKV_PRECISION_16BIT &&
-                           a->head_dim == 256 && a->page_size >= 16
-                       ? 1
-                       : 0;
+  m.ws_row_major = pfkv_partials_row_major(a->precision, a->head_dim, a->page_size, a->num_segments);
   m.merge_sync = nullptr;
   if (a->merge_sync != nullptr) {
     st = check_device_pointer(a->merge_sync, device, "merge_sync");

@@ -161,6 +161,7 @@ def test_partials_layout_by_mode(precision):
     run(case, num_segments=S, workspace=ws, precision=precision)
     torch.cuda.synchronize()
     ml = ws[S * T * Hq * 512:S * T * Hq * 520].view(torch.float32)
+    assert pfkv.partials_row_major(precision, 256, 16, S) == (precision == 0)
     if precision == 0:
         ml = ml.view(T, Hq, S, 2).permute(2, 0, 1, 3)
     else:

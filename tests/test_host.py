@@ -295,3 +295,22 @@ PREFILL_CASES = [
 @pytest.mark.parametrize("name,over,arch,expect", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
 def test_prefill_check_args(lib, name, over, arch, expect):
     assert binding.check_prefill_args(_valid_prefill(**over), arch) == expect, (name, binding.last_error())
+
+
+def test_partials_row_major_table(lib):
+    """Row-major partials exactly for the 16-bit mode at head dim 256 with pages
+    of 16, 32 or 64 tokens and more than 16 segments (up to the 128-segment cap)."""
+    P16, P8P, P8 = binding.PRECISION_16BIT, binding.PRECISION_FP8_P, binding.PRECISION_FP8
+    assert pfkv.partials_row_major(P16, 256, 16, 17)
+    for page in (16, 32, 64):
+        for S in (17, 24, 32, 64, 65, 128):
+            assert pfkv.partials_row_major(P16, 256, page, S), (page, S)
+        for S in (0, 1, 2, 15, 16):
+            assert not pfkv.partials_row_major(P16, 256, page, S), (page, S)
+    for S in (17, 64, 128):
+        assert not pfkv.partials_row_major(P8P, 256, 16, S)
+        assert not pfkv.partials_row_major(P8, 256, 16, S)
+        assert not pfkv.partials_row_major(P16, 128, 16, S)
+        assert not pfkv.partials_row_major(P16, 256, 1, S)
+    for bad in ((P16, 256, 8, 32), (P16, 256, 16, 129), (P16, 192, 16, 32), (7, 256, 16, 32), (-1, 256, 16, 32)):
+        assert not pfkv.partials_row_major(*bad), bad
