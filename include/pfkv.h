@@ -107,9 +107,10 @@ typedef struct pfkv_args {
  * partials under 2 GiB. Other calls run the two launches and leave merge_sync
  * untouched. The result is bit for bit that of the two launches. Measured, it
  * pays at decode (one query token, 16 query heads per work-group, 16
- * segments: 1.2 us of 56 at 16 x 35000) and costs up to about 2% on the
- * other verify shapes (4-token drafts: the merge's synchronization and loads
- * take as long as the launch boundary and the reduce).
+ * segments: 0.8 to 1.2 us of 56 at 16 x 35000) and costs elsewhere: about 2%
+ * on 4-token drafts at up to 16 segments (the merge's synchronization and
+ * loads take as long as the launch boundary and the reduce), 4 to 16% above
+ * 16 segments, where the two launches read row-major partials.
  * The work-groups of a (sequence, head group) count their arrivals in
  * merge_sync; once all have written their partials each merges a share of the
  * group's rows with the reduce's arithmetic. A work-group waits at most
