@@ -260,6 +260,31 @@ def test_single_segment_writes_out_directly():
     assert_parity(full, oracle_for(case), "multigroup S=1 direct")
 
 
+@pytest.mark.parametrize("segments,precision,balance", [(8, 0, False), (24, 0, False), (64, 0, False),
+                                                         (24, 1, False), (40, 0, True)])
+def test_exported_kernels_match_the_call(segments, precision, balance):
+    """pfkv_splitkv_main then pfkv_segment_reduce, called by hand on the same
+    arguments, give the one call's bits, on both partials layouts (segment-major
+    at 8 segments and in the e4m3-P mode, row-major above 16 in the 16-bit mode,
+    balanced or not)."""
+    case = _case("ragged")
+    T, Hq = case.q.shape[0], case.q.shape[1]
+    lib = pfkv.load_library()
+    handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    full = run(case, num_segments=segments, precision=precision) if not balance else pfkv.verify_attn(
+        case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.cu_seqlens_q, case.k_descale,
+        case.v_descale, case.softmax_scale, num_segments=segments, balance_segments=True)
+    ws = torch.zeros(pfkv.workspace_bytes(segments, T, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full_like(case.q, 7.0)
+    args = pfkv.binding.build_args(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                                   case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, segments,
+                                   out, ws, precision, balance_segments=balance)
+    assert lib.pfkv_splitkv_main(ctypes.byref(args), handle) == 0
+    assert lib.pfkv_segment_reduce(ctypes.byref(args), handle) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), full.view(torch.int16))
+
+
 # ------------------------------------------------------------------ closed forms and edge cases
 def _one_sequence(k_codes, v_codes, q, q_len, kd=1.0, vd=1.0, scale=1.0 / 16, hkv=1):
     """Device Case for one sequence with hand-set fp8 codes ([L, Hkv, 256]) and Q values."""
