@@ -247,3 +247,27 @@ def test_prefill_target_shape_sampled(name):
             label = f"{name} head {head} rows {q_lo}..{q_hi}"
             _check(out[q_lo:q_hi, head:head + 1], oracle.prefill_attend(**sub), label, sub)
             _check_lse(lse[head:head + 1, q_lo:q_hi], oracle.prefill_lse(**sub), label)
+
+
+def test_prefill_rows_past_4_gib_bitwise():
+    """K and V rows 1 MiB apart, so that keys from 4096 on sit past the first
+    4 GiB of their buffers (byte offsets above 32 bits): the dense call's bits."""
+    w = PrefillWorkload("far", ((100, 3000), (64, 2200)), 2, 1, True, seed=23)
+    c = make_prefill_case(w, "cpu").to(DEV)
+    dense = _run(c)
+    total_k, stride = c.k.shape[0], 1 << 20
+    assert (total_k - 1) * stride > 1 << 32
+    kb = torch.empty(total_k * stride, dtype=torch.uint8, device=DEV)
+    vb = torch.empty(total_k * stride, dtype=torch.uint8, device=DEV)
+    try:
+        k = kb.as_strided((total_k, 1, 192), (stride, 192, 1))
+        v = vb.as_strided((total_k, 1, 128), (stride, 128, 1))
+        k.copy_(c.k)
+        v.copy_(c.v)
+        far = pfkv.prefill_attn(c.q, k, v, c.q_descale, c.k_descale, c.v_descale, c.cu_seqlens_q, c.cu_seqlens_k,
+                                c.max_seqlen_q, is_causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(far.view(torch.int16), dense.view(torch.int16))
+    finally:
+        del kb, vb
+        torch.cuda.empty_cache()
