@@ -387,6 +387,37 @@ def test_strided_q_and_out():
     assert torch.all(big_out[:, Hq:, :] == 0) and torch.all(big_out[:, :, D:] == 0)
 
 
+def test_q_rows_spanning_just_under_4_gib():
+    """A work-group addresses its Q rows (up to 4 query tokens x its query
+    heads) with 32-bit byte offsets from a 64-bit base, so the call accepts
+    strides whose rows span just under 4 GiB: at that largest stride the result
+    is the contiguous call's, bit for bit; one stride step more is refused."""
+    w = Workload(name="qspan", ctx=(2000, 700), q_lens=(4, 3), num_q_heads=16, num_kv_heads=1,
+                 num_segments=4, seed=35)
+    case = make_case(w, "cpu").to(DEV)
+    T, Hq, D = case.q.shape
+    head = D   # heads of a token contiguous
+    st = (((1 << 32) - 1) // 2 - (Hq - 1) * head - D) // 3 // 8 * 8
+    assert (3 * st + (Hq - 1) * head + D) * 2 < 1 << 32 <= (3 * (st + 8) + (Hq - 1) * head + D) * 2
+    buf = torch.empty((T - 1) * (st + 8) + Hq * head, dtype=torch.bfloat16, device=DEV)
+    try:
+        q = buf.as_strided((T, Hq, D), (st, head, 1))
+        q.copy_(case.q)
+        ref = run(case, num_segments=4)
+        got = pfkv.verify_attn(q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.cu_seqlens_q,
+                               case.k_descale, case.v_descale, case.softmax_scale, num_segments=4)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+        too_far = buf.as_strided((T, Hq, D), (st + 8, head, 1))
+        with pytest.raises(pfkv.PfkvError) as info:
+            pfkv.verify_attn(too_far, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                             case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale, num_segments=4)
+        assert "4 GiB" in str(info.value)
+    finally:
+        del buf
+        torch.cuda.empty_cache()
+
+
 def test_unsupported_group_is_refused():
     w = Workload(name="u", ctx=(64,), q_lens=(4,), num_q_heads=2, num_kv_heads=1, num_segments=1, seed=1)
     case = make_case(w, "cpu").to(DEV)
