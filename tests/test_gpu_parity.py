@@ -111,6 +111,27 @@ def test_full_size_all_rows(name):
     assert_parity(out, ref, f"{name}, all {w.num_seqs} sequences")
 
 
+@pytest.mark.parametrize("n,segments,balance", [(1024, None, False), (1024, 3, False), (200, 16, True)])
+def test_large_decode_batch(n, segments, balance):
+    """Many short sequences (contexts log-uniform in [1, 2000], 1 to 4 query
+    tokens), every row against the oracle: 1024 of them with the heuristic's
+    one segment (N x Hkv above the CU count: the direct path) and with 3
+    segments (3072 work-groups, renumbered over the XCDs); 200 with balanced
+    segments (cap 16), where the 56 slots beyond one per sequence go to the
+    longest contexts."""
+    rng = np.random.default_rng(36)
+    q_lens = tuple(int(x) for x in rng.integers(1, 5, size=n))
+    ctx = tuple(max(int(round(math.exp(rng.uniform(0.0, math.log(2000))))), q) for q in q_lens)
+    w = Workload(name=f"batch{n}", ctx=ctx, q_lens=q_lens, num_q_heads=16, num_kv_heads=1,
+                 num_segments=segments, seed=36)
+    case = make_case(w, "cpu").to(DEV)
+    out = pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.cu_seqlens_q,
+                           case.k_descale, case.v_descale, case.softmax_scale, num_segments=segments,
+                           balance_segments=balance)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), f"{n} sequences S={segments} balanced={balance}")
+
+
 # ------------------------------------------------------------------ workspace partials
 @pytest.mark.parametrize("S", [8, 24])
 def test_segment_partials_match_oracle(S):
