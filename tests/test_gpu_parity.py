@@ -132,6 +132,20 @@ def test_large_decode_batch(n, segments, balance):
     assert_parity(out, oracle_for(case), f"{n} sequences S={segments} balanced={balance}")
 
 
+@pytest.mark.parametrize("segments", [1, None])
+def test_long_single_sequence(segments):
+    """One sequence of 200000 keys and 4 query tokens: at one segment a single
+    work-group streams all 12500 pages (3125 steps, one page-id window refill
+    per 64 steps); at the heuristic's 64 segments the partials are row-major.
+    Every row against the oracle."""
+    w = Workload(name="long1", ctx=(200000,), q_lens=(4,), num_q_heads=16, num_kv_heads=1,
+                 num_segments=segments, seed=37)
+    case = make_case(w, "cpu").to(DEV)
+    out = run(case, num_segments=segments)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_for(case), f"200000 keys S={segments}")
+
+
 # ------------------------------------------------------------------ workspace partials
 @pytest.mark.parametrize("S", [8, 24])
 def test_segment_partials_match_oracle(S):
