@@ -8,7 +8,9 @@
 // (m_s, l_s), lane i dims 4i .. 4i + 3 of the fp16 o rows (head dim 128: lanes
 // 0-31), whose loads for up to 16 segments are in flight together. Above 16
 // segments 2, 4 or (balanced caps above 64) 8 waves share a row; BAL takes each
-// row's segment count from the balanced schedule instead of num_segments.
+// row's segment count from the balanced schedule instead of num_segments; RM
+// reads row-major partials (ws_slot), which the main kernel writes above 16
+// segments in its 16-bit mode at head dim 256.
 #include "segment_merge.h"
 
 namespace pfkv {
