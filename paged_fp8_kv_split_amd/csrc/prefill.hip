@@ -117,19 +117,35 @@ prefill_kernel(PrefillParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
   const int b = blockIdx.z;
-  int hq = blockIdx.y, qt = blockIdx.x;
-  if (CAUSAL) {
+  // Consecutive work-group ids go to the eight XCDs in turn, so a head's tiles
+  // in consecutive ids would run on every XCD and each XCD's L2 would fetch
+  // that head's K and V. xcd_order maps position j of a run of n ids (n a
+  // multiple of 8, the run starting at a multiple of 8) to the order in which
+  // the work is laid out, so that each XCD takes a contiguous eighth of it: a
+  // few heads at a time, their K and V fetched once for that XCD. Otherwise j
+  // itself.
+  auto xcd_order = [](int j, int n) { return (n & 7) == 0 ? (j & 7) * (n >> 3) + (j >> 3) : j; };
+  const int nt = gridDim.x, nh = gridDim.y;
+  // the slice of sequence b starts at a multiple of 8 exactly when nt nh is one
+  const bool aligned = ((nt * nh) & 7) == 0;
+  const int lin = blockIdx.x + nt * blockIdx.y;
+  int hq, qt;
+  if (!CAUSAL) {
+    // head-major: the tiles of one head, then the next
+    const int r = aligned ? xcd_order(lin, nt * nh) : lin;
+    hq = r / nt;
+    qt = r - hq * nt;
+  } else {
     // Causal tiles differ in length (the last query tile sees every key). In
     // dispatch order, the tiles go in kCausalBands bands of decreasing length,
     // each band head-major: long work first and short work last across all
-    // heads (no long tile starts near the end), while the work-groups in
-    // flight still share a band's worth of heads' K/V in the caches.
-    const int nt = gridDim.x, nh = gridDim.y;
-    const int lin = blockIdx.x + nt * blockIdx.y;
+    // heads (no long tile starts near the end). The XCD order applies within a
+    // band, so that every XCD gets the same mix of lengths.
     const int tpb = (nt + kCausalBands - 1) / kCausalBands;   // tiles per band
     const int band = lin / (nh * tpb);
-    const int r = lin - nh * tpb * band;
+    const int j = lin - nh * tpb * band;
     const int sz = min(tpb, nt - band * tpb);                 // tiles in this band
+    const int r = aligned && ((nh * tpb) & 7) == 0 ? xcd_order(j, nh * sz) : j;
     hq = r / sz;
     qt = nt - 1 - (band * tpb + r % sz);                      // rank 0: the longest tile
   }
