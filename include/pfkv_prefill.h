@@ -57,7 +57,7 @@ typedef struct pfkv_prefill_args {
   int32_t num_kv_heads;        /* >= 1 */
   int32_t head_dim_qk;         /* must be 192 */
   int32_t head_dim_v;          /* must be 128 */
-  int32_t max_seqlen_q;        /* bound on every Lq_b, >= 1 */
+  int32_t max_seqlen_q;        /* bound on every Lq_b, >= 1; ceil(max_seqlen_q / 256) * num_q_heads < 2^31 */
   float softmax_scale;         /* finite, > 0 (the usual choice is 1 / sqrt(192)) */
   int32_t causal;              /* 0: full attention; else bottom-right causal */
 } pfkv_prefill_args;

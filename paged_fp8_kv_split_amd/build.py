@@ -29,7 +29,7 @@ KERNEL_SOURCES = ["splitkv_main.hip", "splitkv_main_rm.hip", "splitkv_main_fp8p.
                   "stream_read.hip", "debug_check.hip", "prefill.hip", "noalloc.hip"]
 SOURCES = ["pfkv_host.cpp", *KERNEL_SOURCES]
 # headers the kernel sources include (a change to one rebuilds everything anyway)
-HEADERS = ["pfkv_internal.h", "splitkv_kernel.h", "segment_merge.h"]
+HEADERS = ["pfkv_internal.h", "splitkv_kernel.h", "segment_merge.h", "prefill_config.h"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled for all device code.

@@ -22,6 +22,7 @@
 #include "pfkv.h"
 #include "pfkv_internal.h"
 #include "pfkv_prefill.h"
+#include "prefill_config.h"
 
 namespace {
 
@@ -584,6 +585,10 @@ int pfkv_prefill_check_args(const pfkv_prefill_args* a, const char* arch, int nu
     return fail(PFKV_INVALID, "head counts must be positive (num_q_heads <= 65535)");
   if (a->num_q_heads % a->num_kv_heads != 0) return fail(PFKV_INVALID, "num_q_heads % num_kv_heads != 0");
   if (a->max_seqlen_q < 1 || a->max_seqlen_q > (1 << 30)) return fail(PFKV_INVALID, "max_seqlen_q must be in [1, 2^30]");
+  // the kernel numbers a sequence's (query tile, head) work-groups in 32 bits
+  const int64_t tiles = ((int64_t)a->max_seqlen_q + pfkv::kPrefillTileRows - 1) / pfkv::kPrefillTileRows;
+  if (tiles * a->num_q_heads > INT32_MAX)
+    return fail(PFKV_INVALID, "ceil(max_seqlen_q / 256) * num_q_heads must be below 2^31");
   if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
     return fail(PFKV_INVALID, "softmax_scale must be finite and positive");
   const int64_t byte_strides[] = {a->q_stride_token, a->q_stride_head, a->k_stride_token,

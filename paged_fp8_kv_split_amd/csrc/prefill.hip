@@ -32,6 +32,7 @@
 // * O^T = V^T P^T on the same scaled MFMA (four 32-dim tiles), V^T from LDS by
 //   ds_read_b64_tr_b8, so each lane's accumulators belong to its own row.
 #include "pfkv_internal.h"
+#include "prefill_config.h"
 
 namespace pfkv {
 namespace {
@@ -49,6 +50,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kTileRows = kWaves * kRowsPerWave;      // 256 query rows per work-group
+static_assert(kTileRows == kPrefillTileRows, "the host sizes the grid with kPrefillTileRows");
 constexpr int kKeys = 64;                             // keys per sub-tile
 constexpr int kSubs = 2;                              // sub-tiles per stage
 constexpr int kStageKeys = kSubs * kKeys;             // 128 keys per stage

@@ -281,6 +281,10 @@ PREFILL_CASES = [
     ("heads not divisible", dict(num_kv_heads=7), "gfx950", INVALID),
     ("negative total_k", dict(total_k=-1), "gfx950", INVALID),
     ("zero max_seqlen_q", dict(max_seqlen_q=0), "gfx950", INVALID),
+    ("tiles x heads at 2^31 - 1", dict(max_seqlen_q=(2**31 - 1) // 65535 * 256, num_q_heads=65535,
+                                       num_kv_heads=65535), "gfx950", OK),
+    ("tiles x heads above 2^31 - 1", dict(max_seqlen_q=((2**31 - 1) // 65535 + 1) * 256, num_q_heads=65535,
+                                          num_kv_heads=65535), "gfx950", INVALID),
     ("nan scale", dict(softmax_scale=float("nan")), "gfx950", INVALID),
     ("zero scale", dict(softmax_scale=0.0), "gfx950", INVALID),
     ("q stride not 16", dict(q_stride_head=200), "gfx950", INVALID),
