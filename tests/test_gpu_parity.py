@@ -146,6 +146,44 @@ def test_long_single_sequence(segments):
     assert_parity(out, oracle_for(case), f"200000 keys S={segments}")
 
 
+def _tiled(case: Case, reps: int) -> Case:
+    """reps copies of a problem side by side in one call: copy r has its own
+    pool pages (block tables offset by r pages of the pool) and its own rows."""
+    pages = case.k_cache.shape[0]
+    q_lens = case.cu_seqlens_q[1:] - case.cu_seqlens_q[:-1]
+    cu = torch.zeros(case.seq_lens.numel() * reps + 1, dtype=torch.int32, device=case.q.device)
+    cu[1:] = torch.cumsum(q_lens.repeat(reps), 0)
+    return Case(case.q.repeat(reps, 1, 1), case.k_cache.repeat(reps, 1, 1, 1), case.v_cache.repeat(reps, 1, 1, 1),
+                torch.cat([case.block_tables + r * pages for r in range(reps)]), case.seq_lens.repeat(reps), cu,
+                case.k_descale, case.v_descale, case.softmax_scale, -1, case.workload)
+
+
+@pytest.mark.parametrize("segments", [1, 2])
+def test_more_sequences_than_grid_rows(segments):
+    """70000 sequences: the grid's y dimension (one row per sequence) passes
+    65535. The call is 70 copies of a 1000-sequence problem (contexts 1 to 40,
+    1 to 4 query tokens); every copy's output must equal the first's bit for
+    bit, and the first is checked against the oracle."""
+    rng = np.random.default_rng(38)
+    n, reps = 1000, 70
+    q_lens = tuple(int(x) for x in rng.integers(1, 5, size=n))
+    ctx = tuple(int(max(q, x)) for q, x in zip(q_lens, rng.integers(1, 41, size=n)))
+    w = Workload(name="n1000", ctx=ctx, q_lens=q_lens, num_q_heads=16, num_kv_heads=1, num_segments=segments,
+                 seed=38)
+    one = make_case(w, "cpu").to(DEV)
+    many = _tiled(one, reps)
+    assert many.seq_lens.numel() == n * reps > 65535
+    out = run(many, num_segments=segments)
+    torch.cuda.synchronize()
+    T = one.q.shape[0]
+    first = out[:T]
+    for r in range(1, reps):
+        assert torch.equal(out[r * T:(r + 1) * T].view(torch.int16), first.view(torch.int16)), r
+    assert_parity(first, oracle_for(one), f"70000 sequences S={segments}, first copy")
+    del many, out
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ workspace partials
 @pytest.mark.parametrize("S", [8, 24])
 def test_segment_partials_match_oracle(S):
