@@ -72,17 +72,19 @@ def test_pages_past_4_gib(name, page, hq, hkv, d, segments):
         torch.cuda.empty_cache()
 
 
-def test_pages_past_4_gib_fp8_p():
-    w = Workload(name="far_fp8p", ctx=(3000, 517, 40), q_lens=(4, 2, 1), num_q_heads=16, num_kv_heads=1,
+@pytest.mark.parametrize("precision", [pfkv.binding.PRECISION_FP8_P, pfkv.binding.PRECISION_FP8],
+                         ids=["fp8_p", "fp8_qp"])
+def test_pages_past_4_gib_fp8(precision):
+    w = Workload(name="far_fp8", ctx=(3000, 517, 40), q_lens=(4, 2, 1), num_q_heads=16, num_kv_heads=1,
                  num_segments=8, seed=62)
     near = make_case(w, "cpu").to(DEV)
     far = _far(near)
     try:
-        a = run(near, num_segments=8, precision=pfkv.binding.PRECISION_FP8_P)
-        b = run(far, num_segments=8, precision=pfkv.binding.PRECISION_FP8_P)
+        a = run(near, num_segments=8, precision=precision)
+        b = run(far, num_segments=8, precision=precision)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-        assert_fp8_parity(b, near, pfkv.binding.PRECISION_FP8_P, "far pages fp8 P")
+        assert_fp8_parity(b, near, precision, f"far pages precision {precision}")
     finally:
         del far
         torch.cuda.empty_cache()
