@@ -1,6 +1,7 @@
 """A seeded sweep over combinations of everything the call accepts: query-head
 group, KV heads, ragged query tokens (up to 8), context lengths, cache page
-size, segment count, left window, soft-cap, sinks, arithmetic, lse. Each case
+size, segment count, balanced segments, left window, soft-cap, sinks,
+arithmetic, lse. Each case
 is checked against the oracle at the bar of its arithmetic (16-bit P: max 0.15
 sigma, mean 0.02 sigma, lse within 1e-3; fp8 variants: the fp8 bar of
 gpu_util.assert_fp8_parity). The cases
@@ -25,6 +26,9 @@ DEV = "cuda:0"
 
 def _draw_cases(n=72, seed=2024):
     rng = np.random.default_rng(seed)
+    # balanced segments come from a stream of their own, so that adding them
+    # left every other draw of the earlier cases as it was
+    rng_bal = np.random.default_rng(seed + 1)
     cases = []
     for k in range(n):
         group = int(rng.choice([4, 8, 16, 32]))
@@ -47,9 +51,12 @@ def _draw_cases(n=72, seed=2024):
             # every rounding, so the fp64 model says little about a given case
             ctx = tuple(max(c, 256 + q) for c, q in zip(ctx, q_lens))
             window = -1 if window >= 0 and window < 256 else window
+        balance = bool(rng_bal.random() < 0.3)
+        if balance:
+            segments = max(segments, 2)   # the cap per sequence
         cases.append(dict(id=k, group=group, hkv=hkv, max_q=max_q, q_lens=q_lens, ctx=ctx, page=page,
-                          segments=segments, window=window, softcap=softcap, sinks=sinks, precision=precision,
-                          seed=1000 + k))
+                          segments=segments, balance=balance, window=window, softcap=softcap, sinks=sinks,
+                          precision=precision, seed=1000 + k))
     return cases
 
 
@@ -75,7 +82,8 @@ def test_sweep_case(c):
     out, lse = pfkv.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                                 case.cu_seqlens_q, case.k_descale, case.v_descale, case.softmax_scale,
                                 num_segments=c["segments"], precision=c["precision"], return_lse=True,
-                                sinks=sinks, window_left=c["window"], softcap=c["softcap"], max_q_len=c["max_q"])
+                                sinks=sinks, window_left=c["window"], softcap=c["softcap"], max_q_len=c["max_q"],
+                                balance_segments=c["balance"])
     torch.cuda.synchronize()
     arrs = case.to("cpu").host_arrays()
     opts = dict(window_left=c["window"], softcap=c["softcap"],
