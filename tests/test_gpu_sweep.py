@@ -1,7 +1,7 @@
 """A seeded sweep over combinations of everything the call accepts: query-head
 group, KV heads, ragged query tokens (up to 8), context lengths, cache page
-size, segment count, balanced segments, left window, soft-cap, sinks,
-arithmetic, lse. Each case
+size (one-token pages too), head dim (256 or 128), segment count, balanced
+segments, left window, soft-cap, sinks, arithmetic, lse. Each case
 is checked against the oracle at the bar of its arithmetic (16-bit P: max 0.15
 sigma, mean 0.02 sigma, lse within 1e-3; fp8 variants: the fp8 bar of
 gpu_util.assert_fp8_parity). The cases
@@ -29,6 +29,7 @@ def _draw_cases(n=72, seed=2024):
     # balanced segments come from a stream of their own, so that adding them
     # left every other draw of the earlier cases as it was
     rng_bal = np.random.default_rng(seed + 1)
+    rng_shape = np.random.default_rng(seed + 2)   # head dim 128 and one-token pages, likewise
     cases = []
     for k in range(n):
         group = int(rng.choice([4, 8, 16, 32]))
@@ -54,9 +55,12 @@ def _draw_cases(n=72, seed=2024):
         balance = bool(rng_bal.random() < 0.3)
         if balance:
             segments = max(segments, 2)   # the cap per sequence
+        head_dim = 128 if rng_shape.random() < 0.25 else 256
+        if rng_shape.random() < 0.15:
+            page = 1
         cases.append(dict(id=k, group=group, hkv=hkv, max_q=max_q, q_lens=q_lens, ctx=ctx, page=page,
-                          segments=segments, balance=balance, window=window, softcap=softcap, sinks=sinks,
-                          precision=precision, seed=1000 + k))
+                          segments=segments, balance=balance, head_dim=head_dim, window=window, softcap=softcap,
+                          sinks=sinks, precision=precision, seed=1000 + k))
     return cases
 
 
@@ -73,7 +77,8 @@ def _gpu():
 def test_sweep_case(c):
     print(f"[sweep] {c}", flush=True)
     w = Workload(name=f"sweep{c['id']}", ctx=c["ctx"], q_lens=c["q_lens"], num_q_heads=c["group"] * c["hkv"],
-                 num_kv_heads=c["hkv"], num_segments=c["segments"], seed=c["seed"], page_size=c["page"])
+                 num_kv_heads=c["hkv"], num_segments=c["segments"], seed=c["seed"], page_size=c["page"],
+                 head_dim=c["head_dim"])
     case = make_case(w, "cpu").to(DEV)
     sinks = None
     if c["sinks"]:
