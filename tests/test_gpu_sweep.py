@@ -24,7 +24,7 @@ DEV = "cuda:0"
 
 
 
-def _draw_cases(n=72, seed=2024):
+def _draw_cases(n=144, seed=2024):
     rng = np.random.default_rng(seed)
     # balanced segments come from a stream of their own, so that adding them
     # left every other draw of the earlier cases as it was
