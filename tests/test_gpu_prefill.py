@@ -271,3 +271,32 @@ def test_prefill_rows_past_4_gib_bitwise():
     finally:
         del kb, vb
         torch.cuda.empty_cache()
+
+
+def _draw_prefill_cases(n=32, seed=77):
+    """Seeded combinations: 1 to 4 sequences of 1 to 700 queries over 0 to 1200
+    keys (some with fewer keys than queries), 1 to 4 KV heads with 1 to 4 query
+    heads each, causal or not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        lens = tuple((int(rng.integers(1, 701)), int(rng.integers(0, 1201))) for _ in range(int(rng.integers(1, 5))))
+        hkv = int(rng.integers(1, 5))
+        hq = hkv * int(rng.integers(1, 5))
+        cases.append(dict(id=k, lens=lens, hq=hq, hkv=hkv, causal=bool(rng.integers(0, 2)), seed=500 + k))
+    return cases
+
+
+PREFILL_SWEEP = _draw_prefill_cases()
+
+
+@pytest.mark.parametrize("c", PREFILL_SWEEP, ids=[f"case{c['id']}" for c in PREFILL_SWEEP])
+def test_prefill_sweep_case(c):
+    print(f"[prefill sweep] {c}", flush=True)
+    w = PrefillWorkload(f"sw{c['id']}", c["lens"], c["hq"], c["hkv"], c["causal"], seed=c["seed"])
+    cs = make_prefill_case(w, "cpu").to(DEV)
+    out, lse = _run(cs, return_lse=True)
+    torch.cuda.synchronize()
+    arrs = cs.to("cpu").host_arrays()
+    _check(out, oracle.prefill_attend(**arrs), f"sweep case {c['id']}", arrs)
+    _check_lse(lse, oracle.prefill_lse(**arrs), f"sweep case {c['id']}")
