@@ -47,6 +47,7 @@ N_ROUNDS = 4
 # calls, so that clocks are steady (aiter PR #7375, Performance: 1 s warmup)
 WARMUP_SECONDS = 1.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "splitkv_main_prod_counters.json")
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_12k_counters.json")
 # precision name -> (C ABI value, dtype text)
 PRECISIONS = {
     "16bit": (0, "fp8-e4m3 K/V bytes; bf16 QK and fp16 PV MFMA, fp32 accumulate"),
@@ -74,12 +75,12 @@ def warm_up(fn, min_calls, torch, seconds=WARMUP_SECONDS):
                 return k
 
 
-def kernel_source_digest():
-    """Digest of the main kernel's sources (the templates, the in-launch merge
-    and the 16-bit instantiation) with comments and blank lines removed, so
-    that a change to the code changes it and a change to a comment does not."""
+def _code_digest(names):
+    """sha256[:16] of the named csrc files with comments and blank lines
+    removed, so that a change to the code changes it and a change to a comment
+    does not."""
     h = hashlib.sha256()
-    for name in ("splitkv_kernel.h", "segment_merge.h", "splitkv_main.hip", "splitkv_main_rm.hip", "pfkv_internal.h"):
+    for name in names:
         with open(os.path.join(ROOT, "paged_fp8_kv_split_amd", "csrc", name)) as f:
             text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
         for line in text.splitlines():
@@ -87,6 +88,29 @@ def kernel_source_digest():
             if code.strip():
                 h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest():
+    """Digest of the main kernel's sources (the templates, the in-launch merge
+    and the 16-bit instantiations)."""
+    return _code_digest(("splitkv_kernel.h", "segment_merge.h", "splitkv_main.hip", "splitkv_main_rm.hip",
+                         "pfkv_internal.h"))
+
+
+def prefill_source_digest():
+    """Digest of the prefill kernel's sources."""
+    return _code_digest(("prefill.hip", "prefill_config.h", "pfkv_internal.h"))
+
+
+def prefill_traffic(workload_name, causal):
+    """HBM bytes per prefill launch from committed rocprofv3 counters, if current."""
+    if not os.path.exists(PREFILL_COUNTERS_FILE):
+        return None
+    with open(PREFILL_COUNTERS_FILE) as f:
+        rec = json.load(f)
+    if rec.get("prefill_source_sha256_16") != prefill_source_digest() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("hbm_bytes_per_launch", {}).get("causal" if causal else "non_causal")
 
 
 def measured_traffic(workload_name):
@@ -263,7 +287,7 @@ def bench_prefill(args, pfkv, binding, torch):
                    "device": arch},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 1),
                      "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": prefill_traffic(w.name, w.causal)},
         "variants": {f"causal={not w.causal}": {"us_per_call": round(us_other, 1),
                                                  "value": round(other.flops / (us_other * 1e-6) / 1e12, 2)}},
         "pages_mi450_us": PAGES_PREFILL_US.get(w.name),
